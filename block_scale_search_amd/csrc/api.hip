@@ -1,0 +1,177 @@
+// C ABI (include/nvfp4.h): argument validation on the host, then kernel launches on the
+// caller's stream. Every check runs before anything is enqueued, so argument errors never
+// leave work behind.
+#include <hip/hip_runtime.h>
+
+#include "../../include/nvfp4.h"
+#include "internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+
+int elem_size(int dtype) {
+    if (dtype == NVFP4_DTYPE_F32) return 4;
+    if (dtype == NVFP4_DTYPE_BF16) return 2;
+    return 0;
+}
+
+nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
+
+// Matrix operand [batch, out, in] with row stride ldw and matrix stride stride_w (elements).
+nvfp4_status check_weights(const void* W, int dtype, int64_t batch, int64_t out, int64_t in,
+                           int64_t ldw, int64_t stride_w) {
+    const int esz = elem_size(dtype);
+    if (esz == 0) return NVFP4_ERR_DTYPE;
+    if (batch < 0 || out < 0 || in < 0) return NVFP4_ERR_SHAPE;
+    if (in % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (ldw < in) return NVFP4_ERR_SHAPE;
+    if (batch > 1 && stride_w < out * ldw) return NVFP4_ERR_SHAPE;
+    if (batch > 65535) return NVFP4_ERR_SHAPE;
+    if (out * (in / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+    if (batch == 0 || out == 0 || in == 0) return NVFP4_OK;
+    if (W == nullptr) return NVFP4_ERR_NULL;
+    if (!aligned16(W) || (ldw * esz) % 16 != 0 || (batch > 1 && (stride_w * esz) % 16 != 0))
+        return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* nvfp4_status_string(int status) {
+    switch (status) {
+        case NVFP4_OK: return "NVFP4_OK";
+        case NVFP4_ERR_NULL: return "NVFP4_ERR_NULL: a required pointer is NULL";
+        case NVFP4_ERR_SHAPE: return "NVFP4_ERR_SHAPE: invalid size, leading dimension or stride";
+        case NVFP4_ERR_DTYPE: return "NVFP4_ERR_DTYPE: unknown element type";
+        case NVFP4_ERR_ALIGN: return "NVFP4_ERR_ALIGN: pointer or stride not 16-byte aligned";
+        case NVFP4_ERR_WINDOW: return "NVFP4_ERR_WINDOW: window needs -125 <= lo <= 0 <= hi <= 125";
+        case NVFP4_ERR_ARG: return "NVFP4_ERR_ARG: invalid argument";
+        case NVFP4_ERR_WORKSPACE: return "NVFP4_ERR_WORKSPACE: workspace missing or too small";
+        case NVFP4_ERR_HIP: return "NVFP4_ERR_HIP: HIP runtime error";
+        default: return "NVFP4: unknown status";
+    }
+}
+
+const char* nvfp4_version(void) { return "nvfp4-gfx950 1.0"; }
+
+size_t nvfp4_diag_hessian_workspace_size(int64_t tokens, int64_t in, int64_t segments) {
+    if (tokens < 0 || in < 0 || segments < 1) return 0;
+    return nvfp4::hessian_workspace_bytes(tokens, in, segments);
+}
+
+static nvfp4_status diag_hessian_impl(const void* X, int x_dtype, const int64_t* seg_offsets,
+                                      int64_t segments, int64_t tokens, int64_t in, int64_t ldx,
+                                      double* h_acc, float* h, int accumulate, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+    const int esz = elem_size(x_dtype);
+    if (esz == 0) return NVFP4_ERR_DTYPE;
+    if (tokens < 0 || in < 0 || segments < 1) return NVFP4_ERR_SHAPE;
+    if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (segments > 1 && segments >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
+    if (in == 0) return NVFP4_OK;
+    if (h_acc == nullptr) return NVFP4_ERR_NULL;
+    if (tokens > 0 && X == nullptr) return NVFP4_ERR_NULL;
+    if (seg_offsets == nullptr && segments > 1) return NVFP4_ERR_NULL;
+    if ((X && !aligned16(X)) || !aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u)))
+        return NVFP4_ERR_ALIGN;
+    const int64_t tiles = nvfp4::hessian_max_tiles(tokens, segments);
+    const int64_t col_tiles = (in + 64 * (16 / esz) - 1) / (64 * (16 / esz));
+    if (tiles * col_tiles >= ((int64_t)1 << 31) || tiles >= ((int64_t)1 << 31))
+        return NVFP4_ERR_SHAPE;
+    const size_t need = nvfp4::hessian_workspace_bytes(tokens, in, segments);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_diag_hessian(
+        X, x_dtype == NVFP4_DTYPE_BF16, tokens, in, ldx, segments > 1 ? seg_offsets : nullptr,
+        segments, h_acc, h, accumulate != 0, workspace, static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_diag_hessian(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                int64_t ldx, double* h_acc, float* h, int accumulate,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return diag_hessian_impl(X, x_dtype, nullptr, 1, tokens, in, ldx, h_acc, h, accumulate,
+                             workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_diag_hessian_batched(const void* X, int x_dtype, const int64_t* seg_offsets,
+                                        int64_t segments, int64_t total_tokens, int64_t in,
+                                        int64_t ldx, double* h_acc, float* h, int accumulate,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (segments < 1) return NVFP4_ERR_SHAPE;
+    if (seg_offsets == nullptr) return NVFP4_ERR_NULL;
+    if (segments == 1) {
+        // one segment: its rows are [seg_offsets[0], seg_offsets[1]) = [0, total_tokens)
+        return diag_hessian_impl(X, x_dtype, nullptr, 1, total_tokens, in, ldx, h_acc, h,
+                                 accumulate, workspace, workspace_bytes, stream);
+    }
+    return diag_hessian_impl(X, x_dtype, seg_offsets, segments, total_tokens, in, ldx, h_acc, h,
+                             accumulate, workspace, workspace_bytes, stream);
+}
+
+size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t out, int64_t in) {
+    if (batch < 0 || out < 0 || in < 0) return 0;
+    return nvfp4::global_scale_workspace_bytes(batch, out, in);
+}
+
+nvfp4_status nvfp4_global_scale(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                int64_t in, int64_t ldw, int64_t stride_w, int rule, float* S,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    nvfp4_status st = check_weights(W, w_dtype, batch, out, in, ldw, stride_w);
+    if (st != NVFP4_OK) return st;
+    if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
+    if (batch == 0) return NVFP4_OK;
+    if (S == nullptr) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(S) & 3u) return NVFP4_ERR_ALIGN;
+    const size_t need = nvfp4::global_scale_workspace_bytes(batch, out, in);
+    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 3u) return NVFP4_ERR_ALIGN;
+    // Empty matrices reach the kernels too: the reduction sees no element and S = 1.
+    return hip_status(nvfp4::launch_global_scale(W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in,
+                                                 ldw, stride_w, rule, S, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                int64_t in, int64_t ldw, int64_t stride_w, int32_t group_size,
+                                const float* h, int64_t stride_h, int objective, int32_t lo,
+                                int32_t hi, int exhaustive, const float* S, uint8_t* scales,
+                                uint8_t* packed, float* loss, int8_t* offset, void* stream) {
+    if (group_size != 16) return NVFP4_ERR_ARG;
+    if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
+    if (!exhaustive && (lo > 0 || hi < 0 || lo < -125 || hi > 125)) return NVFP4_ERR_WINDOW;
+    nvfp4_status st = check_weights(W, w_dtype, batch, out, in, ldw, stride_w);
+    if (st != NVFP4_OK) return st;
+    const bool wmse = objective == NVFP4_WMSE;
+    if (wmse) {
+        if (stride_h < 0 || (batch > 1 && stride_h < in) || stride_h % 4 != 0) return NVFP4_ERR_SHAPE;
+    }
+    if (batch == 0 || out == 0 || in == 0) return NVFP4_OK;
+    if (S == nullptr || scales == nullptr || packed == nullptr) return NVFP4_ERR_NULL;
+    if (wmse && h == nullptr) return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(S) & 3u) || !aligned8(packed) ||
+        (loss && (reinterpret_cast<uintptr_t>(loss) & 3u)) || (wmse && !aligned16(h)))
+        return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_scale_search(
+        W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw, stride_w, wmse ? h : nullptr,
+        wmse ? stride_h : 0, wmse, lo, hi, exhaustive != 0, S, scales, packed, loss, offset,
+        static_cast<hipStream_t>(stream)));
+}
+
+nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, int64_t in,
+                        int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
+                        uint8_t* packed, void* stream) {
+    nvfp4_status st = check_weights(W, w_dtype, batch, out, in, ldw, stride_w);
+    if (st != NVFP4_OK) return st;
+    if (batch == 0 || out == 0 || in == 0) return NVFP4_OK;
+    if (S == nullptr || scales == nullptr || packed == nullptr) return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(S) & 3u) || !aligned8(packed)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_pack(W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw,
+                                         stride_w, scales, S, packed,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

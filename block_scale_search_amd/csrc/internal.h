@@ -1,0 +1,36 @@
+// Launchers shared between the C-ABI layer and the kernel files. Arguments are validated by
+// the caller (api.hip); launchers only size grids and enqueue.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Diagonal Hessian: rows per partial tile and the tile count bound used for workspace sizing.
+constexpr int kHessRowsPerTile = 128;
+constexpr int kHessWaves = 16;
+int64_t hessian_max_tiles(int64_t tokens, int64_t segments);
+size_t hessian_workspace_bytes(int64_t tokens, int64_t in, int64_t segments);
+
+hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t in, int64_t ldx,
+                               const int64_t* seg_offsets, int64_t segments, double* h_acc,
+                               float* h, bool accumulate, void* workspace, hipStream_t stream);
+
+size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in);
+hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
+                               hipStream_t stream);
+
+hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
+                               bool wmse, int lo, int hi, bool exhaustive, const float* S,
+                               uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
+                               hipStream_t stream);
+
+hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                       int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
+                       uint8_t* packed, hipStream_t stream);
+
+}  // namespace nvfp4

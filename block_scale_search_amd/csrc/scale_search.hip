@@ -1,0 +1,443 @@
+// Global scale, fused per-group E4M3 scale search + E2M1 quantize + pack, and pack at given
+// scales, for gfx950.
+//
+// Layout: one lane owns one group of 16 consecutive weights of a row (32 B of bf16 or 64 B of
+// f32, two or four 16-byte loads); consecutive lanes own consecutive groups, so a wave reads
+// 2-4 KB of W contiguously and writes 512 B of packed codes and 64 scale bytes contiguously.
+// The per-code table (eff[c], r[c]) of the matrix's global scale sits in LDS and each lane reads
+// the entries of its own candidates.
+//
+// The candidate loop is VALU-bound (there is no contraction to put on MFMA). Per element and
+// candidate it costs one multiply x = |w| * r, half a down-conversion and half an
+// up-conversion (two elements per conversion), the residual fma and, for WMSE, the weighting
+// multiply and the accumulating fma. Codes c and c + 8 are exactly one octave apart
+// (E4M3 mantissa unchanged, exponent + 1), so r[c + 8] = r[c] / 2 and
+// fl(|w| * r[c + 8]) = fl(|w| * r[c]) / 2 exactly; the down-conversion's power-of-two scale
+// operand then rounds x / 2 with no second multiply. Waves whose candidate ranges all sit in
+// the normal codes use that pairing; other waves (clipped windows, subnormal codes, a global
+// scale that breaks the octave identity in binary32) score every code on its own. Both give the
+// same bits. The argmin is lexicographic on (loss, code), which equals "first strictly smaller
+// loss in ascending code order" and lets the paired loop visit codes out of order.
+#include <hip/hip_runtime.h>
+
+#include "device_formats.h"
+#include "internal.h"
+
+namespace nvfp4 {
+namespace {
+
+constexpr int kSearchThreads = 256;
+
+template <bool BF16>
+__device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, float (&w)[16]) {
+    if constexpr (BF16) {
+        const uint4 a = reinterpret_cast<const uint4*>(p)[0];
+        const uint4 b = reinterpret_cast<const uint4*>(p)[1];
+        const uint32_t d[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[2 * i] = bf16_lo(d[i]);
+            w[2 * i + 1] = bf16_hi(d[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = reinterpret_cast<const float4*>(p)[i];
+            w[4 * i] = v.x;
+            w[4 * i + 1] = v.y;
+            w[4 * i + 2] = v.z;
+            w[4 * i + 3] = v.w;
+        }
+    }
+}
+
+// Loss of one code: fixed tree, P_k over elements 4k..4k+3 (first a product, then fmas),
+// L = (P0 + P1) + (P2 + P3).
+template <bool WMSE>
+__device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)[16], float eff,
+                                          float r) {
+    float P[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float x[8], q[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fabsf(w[8 * half + i]) * r;
+        e2m1_round8(x, 1.0f, q);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = 8 * half + i;
+            const float a = fabsf(w[j]);
+            const float d = __builtin_fmaf(-q[i], eff, a);
+            const float u = WMSE ? h[j] * d : d;
+            if ((j & 3) == 0) P[j >> 2] = u * d;
+            else P[j >> 2] = __builtin_fmaf(u, d, P[j >> 2]);
+        }
+    }
+    return (P[0] + P[1]) + (P[2] + P[3]);
+}
+
+// Losses of codes c and c + 8 from one multiply per element (valid when both are normal codes
+// and the table satisfies the octave identity).
+template <bool WMSE>
+__device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)[16], float eff,
+                                          float r, float eff_hi, float& L_lo, float& L_hi) {
+    float P[4], Q[4];
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        float x[8], q[8], s[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = fabsf(w[8 * half + i]) * r;
+        e2m1_round8(x, 1.0f, q);
+        e2m1_round8(x, 2.0f, s);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int j = 8 * half + i;
+            const float a = fabsf(w[j]);
+            const float d = __builtin_fmaf(-q[i], eff, a);
+            const float e = __builtin_fmaf(-s[i], eff_hi, a);
+            const float u = WMSE ? h[j] * d : d;
+            const float v = WMSE ? h[j] * e : e;
+            if ((j & 3) == 0) {
+                P[j >> 2] = u * d;
+                Q[j >> 2] = v * e;
+            } else {
+                P[j >> 2] = __builtin_fmaf(u, d, P[j >> 2]);
+                Q[j >> 2] = __builtin_fmaf(v, e, Q[j >> 2]);
+            }
+        }
+    }
+    L_lo = (P[0] + P[1]) + (P[2] + P[3]);
+    L_hi = (Q[0] + Q[1]) + (Q[2] + Q[3]);
+}
+
+__device__ __forceinline__ void take_min(float L, int c, float& best, int& best_c) {
+    const bool take = (L < best) | ((L == best) & (c < best_c));
+    best = take ? L : best;
+    best_c = take ? c : best_c;
+}
+
+// Per-workgroup code table in LDS: tab[c] = (eff[c], r[c]) for c = 1..126, tab[0] = (0, 0).
+// Returns (uniformly) whether every normal pair (c, c + 8) satisfies eff[c+8] == 2 eff[c] and
+// r[c+8] == r[c] / 2 with r[c] / 2 a normal number.
+__device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
+    const int t = threadIdx.x;
+    if (t == 0) *flag = 0;
+    if (t < 128) {
+        float eff = 0.0f, r = 0.0f;
+        if (t >= 1 && t <= 126) {
+            eff = S * e4m3_value(t);
+            r = __fdiv_rn(1.0f, eff);
+        }
+        tab[t] = make_float2(eff, r);
+    }
+    __syncthreads();
+    if (t >= 8 && t + 8 <= 126) {
+        const float2 a = tab[t], b = tab[t + 8];
+        const bool ok = (b.x == 2.0f * a.x) && (b.y == 0.5f * a.y) && (0.5f * a.y >= 0x1p-126f) &&
+                        (2.0f * a.x < 0x1p127f);
+        if (!ok) atomicOr(flag, 1);
+    }
+    __syncthreads();
+    return *flag == 0;
+}
+
+template <bool BF16, bool WMSE>
+__global__ __launch_bounds__(kSearchThreads) void k_scale_search(
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, int64_t ldw_bytes,
+    int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h, int lo, int hi,
+    int exhaustive, const float* __restrict__ S_arr, uint8_t* __restrict__ scales,
+    uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out) {
+    __shared__ float2 tab[128];
+    __shared__ int flag;
+    const int64_t batch = blockIdx.y;
+    const bool octave_ok = build_table(S_arr[batch], tab, &flag);
+
+    const uint32_t gpr = in >> 4;
+    const uint32_t G = out * gpr;
+    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
+    const bool valid = gi < G;
+    const uint32_t row = valid ? gi / gpr : 0u;
+    const uint32_t g = valid ? gi - row * gpr : 0u;
+
+    float w[16], h[16];
+    if (valid) {
+        load_group<BF16>(W + batch * stride_w_bytes + (int64_t)row * ldw_bytes +
+                             (int64_t)g * (BF16 ? 32 : 64),
+                         w);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) w[j] = 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) h[j] = 0.0f;
+    if (WMSE && valid) {
+        const float4* hp = reinterpret_cast<const float4*>(hvec + batch * stride_h + (int64_t)g * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = hp[i];
+            h[4 * i] = v.x;
+            h[4 * i + 1] = v.y;
+            h[4 * i + 2] = v.z;
+            h[4 * i + 3] = v.w;
+        }
+    }
+
+    // Base code: E4M3 round-to-nearest-even of (absmax / 6) / S, at least 1; 0 = zero group.
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(w[j]));
+    int b = 0;
+    if (amax > 0.0f) {
+        const float s_star = __fdiv_rn(__fdiv_rn(amax, 6.0f), S_arr[batch]);
+        b = max(e4m3_rne_sat(s_star), 1);
+    }
+    const bool live = valid && b > 0;
+
+    // Candidate codes: first + p for p = 0..n-1, kept when inside [1, 126].
+    const int n = exhaustive ? 126 : hi - lo + 1;
+    const int first = exhaustive ? 1 : b + lo;
+    float best = __builtin_inff();
+    int best_c = 255;
+
+    // Paired window path: every live lane's codes lie in 8..126 (no clipping, no subnormal
+    // codes); idle lanes score the in-range dummy range starting at code 8.
+    const bool lane_fast = live ? (first >= 8 && first + n - 1 <= 126) : (n <= 119);
+    if (!exhaustive && octave_ok && __all(lane_fast)) {
+        const int c0 = live ? first : 8;
+        for (int blk = 0; blk < n; blk += 16) {
+            const int nb = min(16, n - blk);
+            for (int p = 0; p < min(nb, 8); ++p) {
+                const int c = c0 + blk + p;
+                const float2 er = tab[c];
+                if (p + 8 < nb) {
+                    float L_lo, L_hi;
+                    loss_pair<WMSE>(w, h, er.x, er.y, tab[c + 8].x, L_lo, L_hi);
+                    take_min(L_lo, c, best, best_c);
+                    take_min(L_hi, c + 8, best, best_c);
+                } else {
+                    take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+                }
+            }
+        }
+    } else if (exhaustive && octave_ok) {
+        // Subnormal codes on their own, then the normal codes 8..126 in octave pairs.
+        for (int c = 1; c < 8; ++c) {
+            const float2 er = tab[c];
+            take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+        }
+        for (int blk = 8; blk <= 126; blk += 16) {
+            const int nb = min(16, 127 - blk);
+            for (int p = 0; p < min(nb, 8); ++p) {
+                const int c = blk + p;
+                const float2 er = tab[c];
+                if (p + 8 < nb) {
+                    float L_lo, L_hi;
+                    loss_pair<WMSE>(w, h, er.x, er.y, tab[c + 8].x, L_lo, L_hi);
+                    take_min(L_lo, c, best, best_c);
+                    take_min(L_hi, c + 8, best, best_c);
+                } else {
+                    take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+                }
+            }
+        }
+    } else {
+        for (int p = 0; p < n; ++p) {
+            const int c = first + p;
+            if (live && c >= 1 && c <= 126) {
+                const float2 er = tab[c];
+                take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+            }
+        }
+    }
+    if (!live) {
+        best = 0.0f;
+        best_c = 0;
+    }
+
+    if (!valid) return;
+    // Quantize once at the chosen code with the weights' signs (tab[0].r = 0 gives signed
+    // zeros for an all-zero group) and pack two nibbles per byte, even element low.
+    const float r = tab[best_c].y;
+    uint32_t p0 = 0u, p1 = 0u;
+    p0 = e2m1_pack2<0>(p0, w[0] * r, w[1] * r);
+    p0 = e2m1_pack2<1>(p0, w[2] * r, w[3] * r);
+    p0 = e2m1_pack2<2>(p0, w[4] * r, w[5] * r);
+    p0 = e2m1_pack2<3>(p0, w[6] * r, w[7] * r);
+    p1 = e2m1_pack2<0>(p1, w[8] * r, w[9] * r);
+    p1 = e2m1_pack2<1>(p1, w[10] * r, w[11] * r);
+    p1 = e2m1_pack2<2>(p1, w[12] * r, w[13] * r);
+    p1 = e2m1_pack2<3>(p1, w[14] * r, w[15] * r);
+    const int64_t gidx = batch * (int64_t)G + gi;
+    reinterpret_cast<uint2*>(packed)[gidx] = make_uint2(p0, p1);
+    scales[gidx] = (uint8_t)best_c;
+    if (loss_out) loss_out[gidx] = best;
+    if (off_out) off_out[gidx] = (int8_t)(best_c - b);
+}
+
+// Quantize + pack at given scale bytes.
+template <bool BF16>
+__global__ __launch_bounds__(kSearchThreads) void k_pack(
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, int64_t ldw_bytes,
+    int64_t stride_w_bytes, const uint8_t* __restrict__ scales, const float* __restrict__ S_arr,
+    uint8_t* __restrict__ packed) {
+    const int64_t batch = blockIdx.y;
+    const uint32_t gpr = in >> 4;
+    const uint32_t G = out * gpr;
+    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
+    if (gi >= G) return;
+    const uint32_t row = gi / gpr, g = gi - row * gpr;
+    const int64_t gidx = batch * (int64_t)G + gi;
+    const int c = scales[gidx];
+    float w[16];
+    load_group<BF16>(W + batch * stride_w_bytes + (int64_t)row * ldw_bytes +
+                         (int64_t)g * (BF16 ? 32 : 64),
+                     w);
+    float r = 0.0f;
+    if (c >= 1 && c <= 126) r = __fdiv_rn(1.0f, S_arr[batch] * e4m3_value(c));
+    uint32_t p0 = 0u, p1 = 0u;
+    p0 = e2m1_pack2<0>(p0, w[0] * r, w[1] * r);
+    p0 = e2m1_pack2<1>(p0, w[2] * r, w[3] * r);
+    p0 = e2m1_pack2<2>(p0, w[4] * r, w[5] * r);
+    p0 = e2m1_pack2<3>(p0, w[6] * r, w[7] * r);
+    p1 = e2m1_pack2<0>(p1, w[8] * r, w[9] * r);
+    p1 = e2m1_pack2<1>(p1, w[10] * r, w[11] * r);
+    p1 = e2m1_pack2<2>(p1, w[12] * r, w[13] * r);
+    p1 = e2m1_pack2<3>(p1, w[14] * r, w[15] * r);
+    reinterpret_cast<uint2*>(packed)[gidx] = make_uint2(p0, p1);
+}
+
+// Global scale, pass 1: max |w| of a slice of rows per workgroup, as the binary32 bit pattern
+// of a non-negative value (ordered like unsigned integers). Exact, order-free.
+constexpr int kAmaxThreads = 256;
+constexpr int kAmaxBlocksPerMatrix = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const uint8_t* __restrict__ W,
+                                                               int64_t out, int64_t in,
+                                                               int64_t ldw_bytes,
+                                                               int64_t stride_w_bytes,
+                                                               uint32_t* __restrict__ partial) {
+    constexpr int C = BF16 ? 8 : 4;  // elements per 16-byte load
+    const int64_t batch = blockIdx.y;
+    const uint8_t* base = W + batch * stride_w_bytes;
+    const int64_t vpr = in / C;  // 16-byte loads per row (in % 16 == 0)
+    // A dense matrix is one long row; otherwise rows are visited one by one.
+    const bool dense = ldw_bytes == vpr * 16;
+    const int64_t rows = dense ? 1 : out;
+    const int64_t row_vec = dense ? out * vpr : vpr;
+    uint32_t m = 0u;
+    const int64_t gtid = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t gsize = (int64_t)gridDim.x * kAmaxThreads;
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint4* rp = reinterpret_cast<const uint4*>(base + r * ldw_bytes);
+        for (int64_t k = gtid; k < row_vec; k += gsize) {
+            const uint4 d = rp[k];
+            if constexpr (BF16) {
+                const uint32_t x[4] = {d.x & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu,
+                                       d.w & 0x7FFF7FFFu};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) m = max(m, max(x[i] << 16, x[i] & 0xFFFF0000u));
+            } else {
+                m = max(m, max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu),
+                               max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu)));
+            }
+        }
+    }
+    // wave reduction, then across the workgroup's waves
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    __shared__ uint32_t wmax[kAmaxThreads / 64];
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = wmax[0];
+        for (int i = 1; i < kAmaxThreads / 64; ++i) r = max(r, wmax[i]);
+        partial[batch * gridDim.x + blockIdx.x] = r;
+    }
+}
+
+// Global scale, pass 2: S = amax / 2688 (448 * 6) or amax / 1536 (256 * 6); 1 if amax = 0.
+__global__ void k_global_scale_finalize(const uint32_t* __restrict__ partial, int64_t nblk,
+                                        int64_t batch, int rule, float* __restrict__ S) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch) return;
+    uint32_t m = 0u;
+    for (int64_t i = 0; i < nblk; ++i) m = max(m, partial[b * nblk + i]);
+    const float amax = __uint_as_float(m);
+    S[b] = amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
+}
+
+int64_t amax_blocks(int64_t out, int64_t in) {
+    const int64_t vec = out * (in / 4);
+    const int64_t want = (vec + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
+    return want < 1 ? 1 : (want > kAmaxBlocksPerMatrix ? kAmaxBlocksPerMatrix : want);
+}
+
+}  // namespace
+
+size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in) {
+    return (size_t)batch * (size_t)amax_blocks(out, in) * sizeof(uint32_t);
+}
+
+hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
+                               hipStream_t stream) {
+    const int64_t nblk = amax_blocks(out, in);
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
+    const int esz = bf16 ? 2 : 4;
+    const dim3 grid((uint32_t)nblk, (uint32_t)batch);
+    if (bf16)
+        hipLaunchKernelGGL(k_amax_partial<true>, grid, dim3(kAmaxThreads), 0, stream,
+                           static_cast<const uint8_t*>(W), out, in, ldw * esz, stride_w * esz,
+                           partial);
+    else
+        hipLaunchKernelGGL(k_amax_partial<false>, grid, dim3(kAmaxThreads), 0, stream,
+                           static_cast<const uint8_t*>(W), out, in, ldw * esz, stride_w * esz,
+                           partial);
+    hipLaunchKernelGGL(k_global_scale_finalize, dim3((uint32_t)((batch + 63) / 64)), dim3(64), 0,
+                       stream, partial, nblk, batch, rule, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
+                               bool wmse, int lo, int hi, bool exhaustive, const float* S,
+                               uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
+                               hipStream_t stream) {
+    const int64_t G = out * (in / 16);
+    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
+    const int esz = bf16 ? 2 : 4;
+    const uint8_t* Wb = static_cast<const uint8_t*>(W);
+#define NVFP4_LAUNCH_SEARCH(B, M)                                                                \
+    hipLaunchKernelGGL((k_scale_search<B, M>), grid, dim3(kSearchThreads), 0, stream, Wb,        \
+                       (uint32_t)out, (uint32_t)in, ldw * esz, stride_w * esz, h, stride_h, lo, \
+                       hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset)
+    if (bf16) {
+        if (wmse) NVFP4_LAUNCH_SEARCH(true, true);
+        else NVFP4_LAUNCH_SEARCH(true, false);
+    } else {
+        if (wmse) NVFP4_LAUNCH_SEARCH(false, true);
+        else NVFP4_LAUNCH_SEARCH(false, false);
+    }
+#undef NVFP4_LAUNCH_SEARCH
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                       int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
+                       uint8_t* packed, hipStream_t stream) {
+    const int64_t G = out * (in / 16);
+    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
+    const int esz = bf16 ? 2 : 4;
+    const uint8_t* Wb = static_cast<const uint8_t*>(W);
+    if (bf16)
+        hipLaunchKernelGGL(k_pack<true>, grid, dim3(kSearchThreads), 0, stream, Wb, (uint32_t)out,
+                           (uint32_t)in, ldw * esz, stride_w * esz, scales, S, packed);
+    else
+        hipLaunchKernelGGL(k_pack<false>, grid, dim3(kSearchThreads), 0, stream, Wb,
+                           (uint32_t)out, (uint32_t)in, ldw * esz, stride_w * esz, scales, S,
+                           packed);
+    return hipGetLastError();
+}
+
+}  // namespace nvfp4

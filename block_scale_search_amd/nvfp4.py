@@ -1,0 +1,246 @@
+"""Thin Python binding of the C ABI in ``include/nvfp4.h`` (ctypes over ``libnvfp4.so``).
+
+Each ``nvfp4_*`` function here has the name and arguments of the C entry point, with torch
+tensors in place of device pointers; it only checks that tensors live on the GPU with the
+expected dtype, contiguity and size, passes their pointers and the current torch stream, and
+raises ``Nvfp4Error`` on a non-OK status. Every computation runs in the library's HIP kernels;
+there is no CPU path. Importing this module fails if the library has not been built
+(``python -m block_scale_search_amd.build``).
+
+The convenience wrappers at the end (``diag_hessian``, ``global_scale``, ``scale_search``,
+``pack``) allocate outputs and workspaces with torch and call the entry points.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m block_scale_search_amd.build`")
+_lib = ctypes.CDLL(_LIB_PATH)
+
+OK, ERR_NULL, ERR_SHAPE, ERR_DTYPE, ERR_ALIGN, ERR_WINDOW, ERR_ARG, ERR_WORKSPACE, ERR_HIP = range(9)
+DTYPE_F32, DTYPE_BF16 = 0, 1
+MSE, WMSE = 0, 1
+GS_AMAX_448, GS_AMAX_256 = 0, 1
+
+_P, _I64, _I32, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
+
+_SIGS = {
+    "nvfp4_status_string": ([_I], ctypes.c_char_p),
+    "nvfp4_version": ([], ctypes.c_char_p),
+    "nvfp4_diag_hessian_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "nvfp4_diag_hessian": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
+    "nvfp4_diag_hessian_batched": ([_P, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
+    "nvfp4_global_scale_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "nvfp4_global_scale": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
+    "nvfp4_scale_search": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I, _I32, _I32, _I,
+                            _P, _P, _P, _P, _P, _P], _I),
+    "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
+}
+for _name, (_args, _res) in _SIGS.items():
+    _f = getattr(_lib, _name)
+    _f.argtypes = _args
+    _f.restype = _res
+
+EXPORTS = tuple(_SIGS)
+
+
+class Nvfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.nvfp4_status_string(status).decode()}")
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Nvfp4Error(status, where)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtypes=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on the GPU")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _wdtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise TypeError(f"unsupported element type {t.dtype} (float32 or bfloat16)")
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t: torch.Tensor, numel: int, name: str):
+    if not t.is_contiguous() or t.numel() < numel:
+        raise ValueError(f"{name} must be contiguous with at least {numel} elements")
+
+
+def nvfp4_version() -> str:
+    return _lib.nvfp4_version().decode()
+
+
+def nvfp4_status_string(status: int) -> str:
+    return _lib.nvfp4_status_string(status).decode()
+
+
+def nvfp4_diag_hessian_workspace_size(tokens: int, inp: int, segments: int = 1) -> int:
+    return int(_lib.nvfp4_diag_hessian_workspace_size(tokens, inp, segments))
+
+
+def nvfp4_global_scale_workspace_size(batch: int, out: int, inp: int) -> int:
+    return int(_lib.nvfp4_global_scale_workspace_size(batch, out, inp))
+
+
+def nvfp4_diag_hessian(X, tokens, inp, ldx, h_acc, h, accumulate, workspace, stream=None):
+    _need(h_acc, inp, "h_acc")
+    if h is not None:
+        _need(h, inp, "h")
+    _check(_lib.nvfp4_diag_hessian(
+        _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx,
+        _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "nvfp4_diag_hessian")
+
+
+def nvfp4_diag_hessian_batched(X, seg_offsets, segments, total_tokens, inp, ldx, h_acc, h,
+                               accumulate, workspace, stream=None):
+    _need(h_acc, segments * inp, "h_acc")
+    if h is not None:
+        _need(h, segments * inp, "h")
+    _check(_lib.nvfp4_diag_hessian_batched(
+        _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X),
+        _dev(seg_offsets, "seg_offsets", (torch.int64,)), segments, total_tokens, inp, ldx,
+        _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), "nvfp4_diag_hessian_batched")
+
+
+def nvfp4_global_scale(W, batch, out, inp, ldw, stride_w, rule, S, workspace, stream=None):
+    _need(S, batch, "S")
+    _check(_lib.nvfp4_global_scale(
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        rule, _dev(S, "S", (torch.float32,)), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)), "nvfp4_global_scale")
+
+
+def nvfp4_scale_search(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h, objective,
+                       lo, hi, exhaustive, S, scales, packed, loss=None, offset=None, stream=None):
+    G = batch * out * (inp // 16)
+    _need(scales, G, "scales")
+    _need(packed, G * 8, "packed")
+    _need(S, batch, "S")
+    if loss is not None:
+        _need(loss, G, "loss")
+    if offset is not None:
+        _need(offset, G, "offset")
+    _check(_lib.nvfp4_scale_search(
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        group_size, _dev(h, "h", (torch.float32,)), stride_h, objective, lo, hi, int(exhaustive),
+        _dev(S, "S", (torch.float32,)), _dev(scales, "scales", (torch.uint8,)),
+        _dev(packed, "packed", (torch.uint8,)), _dev(loss, "loss", (torch.float32,)),
+        _dev(offset, "offset", (torch.int8,)), _stream(stream)), "nvfp4_scale_search")
+
+
+def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None):
+    G = batch * out * (inp // 16)
+    _need(scales, G, "scales")
+    _need(packed, G * 8, "packed")
+    _check(_lib.nvfp4_pack(
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        _dev(scales, "scales", (torch.uint8,)), _dev(S, "S", (torch.float32,)),
+        _dev(packed, "packed", (torch.uint8,)), _stream(stream)), "nvfp4_pack")
+
+
+# --- convenience wrappers (allocate outputs with torch, then call the entry points) ----------
+
+def _bmat(W: torch.Tensor):
+    """(batch, out, in, ldw, stride_w) of a [out, in] or [batch, out, in] row-major tensor."""
+    if W.dim() == 2:
+        if W.stride(1) != 1:
+            raise ValueError("W rows must be contiguous")
+        return 1, W.shape[0], W.shape[1], W.stride(0), W.shape[0] * W.stride(0)
+    if W.dim() == 3:
+        if W.stride(2) != 1:
+            raise ValueError("W rows must be contiguous")
+        return W.shape[0], W.shape[1], W.shape[2], W.stride(1), W.stride(0)
+    raise ValueError("W must be 2-D or 3-D")
+
+
+def diag_hessian(X: torch.Tensor, h_acc: torch.Tensor | None = None, accumulate: bool = False,
+                 stream=None):
+    """h over X [tokens, in]; returns (h_acc float64 [in], h float32 [in])."""
+    T, n = X.shape
+    if X.stride(1) != 1:
+        raise ValueError("X rows must be contiguous")
+    if h_acc is None:
+        h_acc = torch.zeros(n, dtype=torch.float64, device=X.device)
+    h = torch.empty(n, dtype=torch.float32, device=X.device)
+    ws = torch.empty(max(1, nvfp4_diag_hessian_workspace_size(T, n, 1)), dtype=torch.uint8,
+                     device=X.device)
+    nvfp4_diag_hessian(X, T, n, X.stride(0), h_acc, h, accumulate, ws, stream)
+    return h_acc, h
+
+
+def diag_hessian_batched(X: torch.Tensor, seg_offsets: torch.Tensor,
+                         h_acc: torch.Tensor | None = None, accumulate: bool = False, stream=None):
+    """Per-segment h over the routed rows of X; returns (h_acc [E, in] f64, h [E, in] f32)."""
+    T, n = X.shape
+    E = seg_offsets.numel() - 1
+    if h_acc is None:
+        h_acc = torch.zeros((E, n), dtype=torch.float64, device=X.device)
+    h = torch.empty((E, n), dtype=torch.float32, device=X.device)
+    ws = torch.empty(max(1, nvfp4_diag_hessian_workspace_size(T, n, E)), dtype=torch.uint8,
+                     device=X.device)
+    nvfp4_diag_hessian_batched(X, seg_offsets, E, T, n, X.stride(0), h_acc, h, accumulate, ws,
+                               stream)
+    return h_acc, h
+
+
+def global_scale(W: torch.Tensor, rule: int = GS_AMAX_448, stream=None) -> torch.Tensor:
+    b, o, n, ldw, sw = _bmat(W)
+    S = torch.empty(b, dtype=torch.float32, device=W.device)
+    ws = torch.empty(max(1, nvfp4_global_scale_workspace_size(b, o, n)), dtype=torch.uint8,
+                     device=W.device)
+    nvfp4_global_scale(W, b, o, n, ldw, sw, rule, S, ws, stream)
+    return S
+
+
+def scale_search(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objective: int,
+                 lo: int = -9, hi: int = 6, exhaustive: bool = False, with_stats: bool = True,
+                 stream=None):
+    """Scale search + pack over W [out, in] or [batch, out, in]; h [in] or [batch, in]."""
+    b, o, n, ldw, sw = _bmat(W)
+    shp = (o, n // 16) if W.dim() == 2 else (b, o, n // 16)
+    dev = W.device
+    scales = torch.empty(shp, dtype=torch.uint8, device=dev)
+    packed = torch.empty(shp[:-1] + (n // 2,), dtype=torch.uint8, device=dev)
+    loss = torch.empty(shp, dtype=torch.float32, device=dev) if with_stats else None
+    offset = torch.empty(shp, dtype=torch.int8, device=dev) if with_stats else None
+    stride_h = 0
+    if objective == WMSE:
+        if h is None:
+            raise ValueError("WMSE needs h")
+        stride_h = h.stride(0) if h.dim() == 2 else 0
+    nvfp4_scale_search(W, b, o, n, ldw, sw, 16, h if objective == WMSE else None, stride_h,
+                       objective, lo, hi, exhaustive, S, scales, packed, loss, offset, stream)
+    return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def pack(W: torch.Tensor, scales: torch.Tensor, S: torch.Tensor, stream=None) -> torch.Tensor:
+    b, o, n, ldw, sw = _bmat(W)
+    packed = torch.empty(scales.shape[:-1] + (n // 2,), dtype=torch.uint8, device=W.device)
+    nvfp4_pack(W, b, o, n, ldw, sw, scales, S, packed, stream)
+    return packed

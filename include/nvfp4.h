@@ -1,0 +1,172 @@
+/*
+ * nvfp4.h - C ABI of the MI355X (gfx950) NVFP4 per-group E4M3 block-scale search library.
+ *
+ * The library computes, on one GPU, the data-parallel core shared by the NVFP4 scale-refinement
+ * methods described in
+ *   [HS] "H-Scale: Hessian-Guided Scale Refinement for NVFP4 Sub-Byte LLM Inference",
+ *   [SS] "ScaleSweep" (technical summary), and the scale step of
+ *   [SR] "Replay the Curvature: Accurate and Scalable NVFP4 Quantization for LLM Inference":
+ *   1. a diagonal second-order weight h_j = sum_t x_tj^2 from calibration activations X;
+ *   2. a global FP32 scale S per tensor;
+ *   3. for every group of 16 consecutive weights of a row, the E4M3 local scale chosen from a
+ *      window of adjacent E4M3 codes around the rounded absmax/6 base (or from all 126 codes)
+ *      by E2M1 round-to-nearest-even quantization and the h-weighted (or plain) squared error;
+ *   4. the packed 4-bit codes and the E4M3 scale bytes.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer named "device" is GPU memory owned by the caller; the library allocates
+ *     nothing and keeps no state between calls. Host pointers are named as such.
+ *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
+ *     asynchronous. Argument errors are detected on the host and returned before anything is
+ *     enqueued; a failed kernel launch returns NVFP4_ERR_HIP. Nothing is thrown across the ABI.
+ *   - Matrices are row-major. Sizes and leading dimensions are in elements. A matrix argument
+ *     with a zero dimension is valid and enqueues no work (except where noted).
+ *   - Inputs must be finite; results for non-finite inputs are unspecified.
+ *   - Results are deterministic: identical inputs give byte-identical outputs (no float atomics).
+ *   - Calls that overlap on the same output buffers race; the library does not serialise them.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum nvfp4_status {
+    NVFP4_OK = 0,
+    NVFP4_ERR_NULL = 1,      /* a required pointer is NULL */
+    NVFP4_ERR_SHAPE = 2,     /* negative size, in % 16 != 0, ld < in, size too large, ... */
+    NVFP4_ERR_DTYPE = 3,     /* unknown element type */
+    NVFP4_ERR_ALIGN = 4,     /* a pointer, stride or leading dimension breaks 16-byte rows */
+    NVFP4_ERR_WINDOW = 5,    /* window with lo > 0, hi < 0 or |lo|, |hi| > 125 */
+    NVFP4_ERR_ARG = 6,       /* other invalid argument (objective, rule, group size, ...) */
+    NVFP4_ERR_WORKSPACE = 7, /* workspace missing or smaller than the *_workspace_size value */
+    NVFP4_ERR_HIP = 8        /* a HIP runtime call or kernel launch failed */
+} nvfp4_status;
+
+typedef enum nvfp4_dtype { NVFP4_DTYPE_F32 = 0, NVFP4_DTYPE_BF16 = 1 } nvfp4_dtype;
+
+/* [SS] Methodology §1: MSE (plain reconstruction error) and WMSE (weighted by importance
+ * scores from activation statistics); [HS] §3: the diagonal-Hessian-weighted objective. */
+typedef enum nvfp4_objective { NVFP4_MSE = 0, NVFP4_WMSE = 1 } nvfp4_objective;
+
+/* Global-scale rule. [SS] Methodology §2 fixes S = max|w| / (256 * 6) (NVFP4_GS_AMAX_256).
+ * NVFP4_GS_AMAX_448 maps the largest group onto E4M3's largest finite value:
+ * S = max|w| / (448 * 6). An all-zero tensor gets S = 1. */
+typedef enum nvfp4_gs_rule { NVFP4_GS_AMAX_448 = 0, NVFP4_GS_AMAX_256 = 1 } nvfp4_gs_rule;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* nvfp4_status_string(int status);
+
+/* Library version string, e.g. "nvfp4-gfx950 1.0". */
+const char* nvfp4_version(void);
+
+/* ---------------------------------------------------------------------------------------------
+ * Step 1: diagonal second-order weight ([HS] §3 and App. B: h = diag(X^T X) from calibration
+ * activations, cross-channel terms dropped; [SS] §1: Gram-matrix diagonals as WMSE importance;
+ * [SR] §3: H from the calibration inputs).
+ *
+ *   h_acc[j] = (accumulate ? h_acc[j] : 0) + sum_{t < tokens} X[t, j]^2     (binary64)
+ *   h[j]     = (float) h_acc[j]                                              (round to nearest)
+ *
+ * X       device, [tokens, in] with row stride ldx, bf16 or f32 (x_dtype), 16-byte aligned.
+ * h_acc   device, [in] binary64 running sum; read when accumulate != 0, always written. Keeping
+ *         it across calls streams X in token chunks with no intermediate fp32 rounding.
+ * h       device, [in] binary32 output; may be NULL.
+ * workspace  device scratch of at least nvfp4_diag_hessian_workspace_size(tokens, in, 1) bytes,
+ *         16-byte aligned; its contents are overwritten and need no initialisation.
+ * Requires in % 8 == 0 and ldx % 8 == 0. tokens == 0 is valid: h_acc is cleared (accumulate
+ * == 0) or kept, and h is written from it. Partial sums are combined in a fixed order, so the
+ * result does not depend on scheduling.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_diag_hessian_workspace_size(int64_t tokens, int64_t in, int64_t segments);
+
+nvfp4_status nvfp4_diag_hessian(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                int64_t ldx, double* h_acc, float* h, int accumulate,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Batched form for a mixture-of-experts layer: X holds the routed tokens of `segments` experts
+ * back to back; expert e owns rows [seg_offsets[e], seg_offsets[e+1]). Writes h_acc/h as
+ * [segments, in] (row e = expert e), with the same accumulate rule per row.
+ * seg_offsets  device, int64 [segments + 1], non-decreasing, seg_offsets[0] == 0 and
+ *              seg_offsets[segments] == total_tokens (not checked on the device).
+ * workspace    at least nvfp4_diag_hessian_workspace_size(total_tokens, in, segments) bytes. */
+nvfp4_status nvfp4_diag_hessian_batched(const void* X, int x_dtype, const int64_t* seg_offsets,
+                                        int64_t segments, int64_t total_tokens, int64_t in,
+                                        int64_t ldx, double* h_acc, float* h, int accumulate,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Step 2: global FP32 scale per tensor ([HS] §3: a tensor-level FP32 global scale, the effective
+ * group scale being the product of global and local scales; [SS] §2: S = max|x| / (256 * 6)).
+ *
+ * W        device, `batch` matrices [out, in], row stride ldw, matrix stride stride_w (elements),
+ *          bf16 or f32, 16-byte aligned rows.
+ * S        device, float [batch]: S[b] from the max |w| of matrix b by `rule`.
+ * workspace  device scratch of nvfp4_global_scale_workspace_size(batch, out, in) bytes.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t out, int64_t in);
+
+nvfp4_status nvfp4_global_scale(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                int64_t in, int64_t ldw, int64_t stride_w, int rule, float* S,
+                                void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Steps 3-4: per-group E4M3 scale search, fused with quantize + pack.
+ *
+ * For group g of 16 consecutive input columns of row o of matrix b ([HS] §3 and [SR] §4.1.1:
+ * groups of 16, one E4M3 local scale per group):
+ *   eff[c] = fl(S[b] * E4M3(c)), r[c] = fl(1 / eff[c])           for codes c = 1..126
+ *   base   = E4M3 round-to-nearest-even of fl(fl(max|w| / 6) / S[b]), saturating at 448, and
+ *            raised to code 1 if it rounds to 0 ([SS] Problem Statement and §2: AbsMax start,
+ *            s_base = FP8-rounded block maximum; [HS] §4: max-abs initialisation)
+ *   codes  = base + lo .. base + hi clipped to [1, 126] ([HS] §3: nine smaller and six larger
+ *            E4M3 steps with endpoint clipping; [SS] §3: offsets [-3, 7] for MSE, [-8, 7] for
+ *            WMSE in FP8 bit-pattern space), or all codes 1..126 if exhaustive ([SS] §2)
+ *   loss(c) = sum_j u_j * d_j, x_j = fl(|w_j| * r[c]), q_j = E2M1_RNE(x_j) (ties to the even
+ *            code, saturating at 6), d_j = fma(-q_j, eff[c], |w_j|), u_j = fl(h_j * d_j) for
+ *            WMSE or d_j for MSE, summed as four fma chains over j = 4k..4k+3 then
+ *            (P0 + P1) + (P2 + P3) in binary32
+ *   choice = the code of smallest loss, the lowest code among equal losses ([SR] App. D.2:
+ *            ties are deterministic)
+ *   output ([HS] App. B: quantize once with the chosen scale, native NVFP4):
+ *            scales[b, o, g] = chosen code (0 for an all-zero group)
+ *            packed[b, o, 8g + k] = nibble(2k) | nibble(2k+1) << 4, nibble = sign(w) << 3 |
+ *            E2M1 index of fl(|w| * r[choice])
+ *            loss[b, o, g] = loss(choice) (0 for a zero group), offset[b, o, g] = choice - base
+ *
+ * W         device, `batch` matrices [out, in] (ldw, stride_w in elements), bf16 or f32,
+ *           16-byte aligned rows (ldw, stride_w multiples of 16 bytes).
+ * group_size must be 16.
+ * h         device, float [batch, in] with row stride stride_h (multiple of 4), 16-byte
+ *           aligned; required for WMSE, ignored (may be NULL) for MSE.
+ * lo, hi    window offsets, -125 <= lo <= 0 <= hi <= 125; ignored when exhaustive != 0.
+ * S         device, float [batch], positive, finite, with every S * E4M3(c) a normal binary32
+ *           value whose reciprocal is finite (otherwise results are unspecified).
+ * scales    device, uint8 [batch, out, in/16];  packed  device, uint8 [batch, out, in/2].
+ * loss      device, float [batch, out, in/16] or NULL; offset device, int8 [...] or NULL.
+ * Requires in % 16 == 0 and batch * ... sizes with out * in/16 < 2^31 per matrix.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                int64_t in, int64_t ldw, int64_t stride_w, int32_t group_size,
+                                const float* h, int64_t stride_h, int objective, int32_t lo,
+                                int32_t hi, int exhaustive, const float* S, uint8_t* scales,
+                                uint8_t* packed, float* loss, int8_t* offset, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Quantize + pack at given scale bytes ([HS] App. B: the group is quantized once with its
+ * scale; round-to-nearest at a fixed scale). Same layouts and nibble rule as above; a scale
+ * byte of 0 gives signed zero codes. Scale bytes must be 0..126.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, int64_t in,
+                        int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
+                        uint8_t* packed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

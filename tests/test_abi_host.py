@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every entry point its header declares, and rejects bad
+arguments on the host before anything is enqueued (CPU only: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+LIB = os.path.join(ROOT, "block_scale_search_amd", "libnvfp4.so")
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libnvfp4.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for want in ("nvfp4_diag_hessian", "nvfp4_diag_hessian_batched", "nvfp4_global_scale",
+                 "nvfp4_scale_search", "nvfp4_pack", "nvfp4_status_string",
+                 "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing
+
+
+def test_binding_covers_every_symbol():
+    from block_scale_search_amd import nvfp4
+    assert set(_declared()) <= set(nvfp4.EXPORTS)
+    assert nvfp4.nvfp4_version().startswith("nvfp4-gfx950")
+    for s in range(9):
+        assert nvfp4.nvfp4_status_string(s).startswith("NVFP4_")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from block_scale_search_amd import nvfp4
+    return nvfp4._lib
+
+
+FAKE = ctypes.c_void_p(1 << 20)       # 16-byte aligned, never dereferenced: calls fail first
+ODD = ctypes.c_void_p((1 << 20) + 4)
+
+
+def _search(lib, **kw):
+    a = dict(W=FAKE, dt=1, batch=1, out=4, inp=64, ldw=64, sw=256, gs=16, h=FAKE, sh=0, obj=1,
+             lo=-9, hi=6, exh=0, S=FAKE, sc=FAKE, pk=FAKE, loss=None, off=None)
+    a.update(kw)
+    return lib.nvfp4_scale_search(a["W"], a["dt"], a["batch"], a["out"], a["inp"], a["ldw"],
+                                  a["sw"], a["gs"], a["h"], a["sh"], a["obj"], a["lo"], a["hi"],
+                                  a["exh"], a["S"], a["sc"], a["pk"], a["loss"], a["off"], None)
+
+
+def test_scale_search_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    assert _search(lib, gs=32) == n.ERR_ARG
+    assert _search(lib, obj=7) == n.ERR_ARG
+    assert _search(lib, dt=5) == n.ERR_DTYPE
+    assert _search(lib, inp=40, ldw=40) == n.ERR_SHAPE            # in % 16 != 0
+    assert _search(lib, ldw=32) == n.ERR_SHAPE                    # ld < in
+    assert _search(lib, out=-1) == n.ERR_SHAPE
+    assert _search(lib, lo=1) == n.ERR_WINDOW
+    assert _search(lib, hi=-1) == n.ERR_WINDOW
+    assert _search(lib, lo=-126) == n.ERR_WINDOW
+    assert _search(lib, hi=126) == n.ERR_WINDOW
+    assert _search(lib, W=None) == n.ERR_NULL
+    assert _search(lib, h=None) == n.ERR_NULL                     # WMSE needs h
+    assert _search(lib, S=None) == n.ERR_NULL
+    assert _search(lib, W=ODD) == n.ERR_ALIGN
+    assert _search(lib, ldw=68) == n.ERR_ALIGN                    # bf16 rows of 136 bytes
+    assert _search(lib, batch=2, sw=100) == n.ERR_SHAPE           # matrices overlap
+    assert _search(lib, out=1 << 26, inp=1 << 10, ldw=1 << 10) == n.ERR_SHAPE
+    # empty problems are valid and enqueue nothing
+    assert _search(lib, out=0) == n.OK
+    assert _search(lib, batch=0) == n.OK
+    assert _search(lib, inp=0, ldw=0) == n.OK
+    # an exhaustive search ignores the window
+    assert _search(lib, exh=1, lo=5, hi=-5, W=None) == n.ERR_NULL
+
+
+def test_pack_and_global_scale_reject_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    assert lib.nvfp4_pack(FAKE, 1, 1, 4, 40, 40, 160, FAKE, FAKE, FAKE, None) == n.ERR_SHAPE
+    assert lib.nvfp4_pack(FAKE, 1, 1, 4, 64, 64, 256, None, FAKE, FAKE, None) == n.ERR_NULL
+    assert lib.nvfp4_pack(FAKE, 9, 1, 4, 64, 64, 256, FAKE, FAKE, FAKE, None) == n.ERR_DTYPE
+    assert lib.nvfp4_pack(FAKE, 1, 1, 0, 64, 64, 0, None, None, None, None) == n.OK
+    assert lib.nvfp4_global_scale(FAKE, 1, 1, 4, 64, 64, 256, 3, FAKE, FAKE, 1 << 20, None) == n.ERR_ARG
+    assert lib.nvfp4_global_scale(FAKE, 1, 1, 4, 64, 64, 256, 0, None, FAKE, 1 << 20, None) == n.ERR_NULL
+    assert lib.nvfp4_global_scale(FAKE, 1, 1, 4, 64, 64, 256, 0, FAKE, None, 0, None) == n.ERR_WORKSPACE
+    assert lib.nvfp4_global_scale(FAKE, 1, 0, 4, 64, 64, 256, 0, None, None, 0, None) == n.OK
+
+
+def test_diag_hessian_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    ws = lib.nvfp4_diag_hessian_workspace_size(1000, 64, 1)
+    assert ws >= 8 * 8 * 64                                        # ceil(1000/128) tiles of fp64
+    assert lib.nvfp4_diag_hessian_workspace_size(-1, 64, 1) == 0
+    assert lib.nvfp4_diag_hessian_workspace_size(1000, 64, 4) > ws  # + per-expert tiles
+    H = lib.nvfp4_diag_hessian
+    assert H(FAKE, 1, 1000, 60, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_SHAPE    # in % 8
+    assert H(FAKE, 1, 1000, 64, 60, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_SHAPE    # ldx < in
+    assert H(FAKE, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_DTYPE
+    assert H(None, 1, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_NULL
+    assert H(FAKE, 1, 1000, 64, 64, None, FAKE, 0, FAKE, ws, None) == n.ERR_NULL
+    assert H(FAKE, 1, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws - 1, None) == n.ERR_WORKSPACE
+    assert H(FAKE, 1, 1000, 64, 64, FAKE, FAKE, 0, None, ws, None) == n.ERR_WORKSPACE
+    assert H(ODD, 1, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_ALIGN
+    assert H(FAKE, 1, 1000, 0, 0, None, None, 0, None, 0, None) == n.OK             # in == 0
+    B = lib.nvfp4_diag_hessian_batched
+    wsb = lib.nvfp4_diag_hessian_workspace_size(1000, 64, 4)
+    assert B(FAKE, 1, None, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, wsb, None) == n.ERR_NULL
+    assert B(FAKE, 1, FAKE, 0, 1000, 64, 64, FAKE, FAKE, 0, FAKE, wsb, None) == n.ERR_SHAPE
+    assert B(FAKE, 1, FAKE, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_WORKSPACE

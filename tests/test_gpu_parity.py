@@ -1,0 +1,285 @@
+"""GPU parity: the HIP library (through the C ABI) against the CPU oracle, element by element.
+
+Bar: scale bytes, packed codes and offsets bit-exact; losses bit-exact (same binary32 ops in the
+same order); h within 1e-5 relative (in practice equal: both sum in binary64 and round once).
+Sizes span several workgroups and ragged tails; the edge cases cover empty inputs, all-zero
+groups, signed zeros, clipped windows at both ends of the code range, subnormal codes,
+zero and wide-range h, and batched matrices.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scale_search_amd import workloads
+
+pytestmark = pytest.mark.gpu
+
+H_RTOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def nv():
+    from block_scale_search_amd import nvfp4
+    return nvfp4
+
+
+DEV = "cuda"
+
+
+def host_w(W: torch.Tensor) -> np.ndarray:
+    """W as the oracle takes it: float32, or bf16 bit patterns as uint16."""
+    W = W.detach().cpu().contiguous()
+    if W.dtype == torch.bfloat16:
+        return W.view(torch.int16).numpy().view(np.uint16)
+    return W.numpy().astype(np.float32)
+
+
+OBJ = {"mse": oracle.MSE, "wmse": oracle.WMSE}
+
+
+def oracle_search(W: torch.Tensor, h, S, objective, lo, hi, exhaustive):
+    """Oracle over [out, in] or [batch, out, in]; h [in] / [batch, in] numpy; S list."""
+    Wn = host_w(W)
+    if Wn.ndim == 2:
+        Wn, h, S = Wn[None], None if h is None else h[None], [S] if np.isscalar(S) else S
+    res = [oracle.scale_search(Wn[b], None if h is None else h[b], OBJ[objective], lo, hi,
+                               exhaustive, float(S[b])) for b in range(Wn.shape[0])]
+    return {k: np.stack([r[k] for r in res]) for k in res[0]}
+
+
+def gpu_search(nv, W, h, S, objective, lo, hi, exhaustive):
+    r = nv.scale_search(W, h, S, nv.WMSE if objective == "wmse" else nv.MSE, lo, hi, exhaustive)
+    torch.cuda.synchronize()
+    out = {k: v.cpu().numpy() for k, v in r.items()}
+    if W.dim() == 2:
+        out = {k: v[None] for k, v in out.items()}
+    return out
+
+
+def assert_same(g, o, what=""):
+    for k in ("scales", "offset", "loss", "packed"):
+        a, b = g[k], o[k]
+        if k == "loss":
+            a, b = a.view(np.uint32), b.view(np.uint32)
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, f"{what} {k}: {len(bad)} mismatches, first at {bad[:3].tolist()}"
+
+
+def _mat(out, inp, dtype, seed, outlier=0.003, batch=None):
+    W = workloads.normal_weights(out, inp, 0.02, outlier, 25.0, seed, DEV, dtype, batch=batch)
+    return W
+
+
+def _h(inp, seed, batch=None, spread=2.0):
+    g = torch.Generator(device=DEV)
+    g.manual_seed(seed)
+    shape = (inp,) if batch is None else (batch, inp)
+    return torch.exp(torch.randn(shape, generator=g, device=DEV) * spread).float()
+
+
+# ---------------------------------------------------------------------------------------------
+
+def test_tiny_layer_all_modes(nv):
+    """The tiny layer (W 256x256 fp32, X 512x256 bf16): h, S, every mode, bit-exact."""
+    cfg = workloads.CONFIGS["tiny"]
+    W = workloads.make_weights(cfg, DEV)
+    sig = workloads.make_sigma(cfg, DEV)
+    X, _ = workloads.make_activation_chunk(cfg, sig, 0, DEV)
+    h_acc, h = nv.diag_hessian(X)
+    acc_o, h_o = oracle.diag_hessian(host_w(X))
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    np.testing.assert_allclose(h_acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    S_o = oracle.global_scale(host_w(W), oracle.GS_AMAX_448)
+    assert S.item() == np.float32(S_o)
+    hn = h.cpu().numpy()
+    for mode in cfg.modes + [workloads.Mode("mse", exhaustive=True), workloads.Mode("wmse", -8, 7)]:
+        g = gpu_search(nv, W, h if mode.objective == "wmse" else None, S, mode.objective,
+                       mode.lo, mode.hi, mode.exhaustive)
+        o = oracle_search(W, hn if mode.objective == "wmse" else None, S_o, mode.objective,
+                          mode.lo, mode.hi, mode.exhaustive)
+        assert_same(g, o, mode.label)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("shape", [(1, 37, 16), (1, 129, 48), (1, 300, 272), (3, 67, 160),
+                                   (1, 5, 4096)])
+def test_ragged_shapes(nv, dtype, shape):
+    b, out, inp = shape
+    W = _mat(out, inp, dtype, seed=out + inp, batch=None if b == 1 else b)
+    h = _h(inp, seed=inp, batch=None if b == 1 else b)
+    S = nv.global_scale(W, nv.GS_AMAX_256)
+    Sn = S.cpu().numpy().reshape(-1)
+    hn = h.cpu().numpy()
+    for obj, lo, hi, exh in (("wmse", -9, 6, False), ("mse", -3, 7, False), ("wmse", -8, 7, False),
+                             ("wmse", 0, 0, True)):
+        g = gpu_search(nv, W, h if obj == "wmse" else None, S, obj, lo, hi, exh)
+        o = oracle_search(W, hn if obj == "wmse" else None, Sn, obj, lo, hi, exh)
+        assert_same(g, o, f"{shape} {obj} [{lo},{hi}] exh={exh}")
+
+
+def test_padded_rows_and_strided_batch(nv):
+    """ldw > in and a matrix stride larger than out * ldw: only the logical elements count."""
+    base = _mat(40, 256, torch.bfloat16, seed=5, batch=2)
+    big = torch.full((2, 48, 320), 7.0, dtype=torch.bfloat16, device=DEV)  # padding would win
+    big[:, :40, :256] = base
+    view = big[:, :40, :256]
+    h = _h(256, seed=6, batch=2)
+    S = nv.global_scale(view, nv.GS_AMAX_448)
+    assert torch.equal(S, nv.global_scale(base.contiguous(), nv.GS_AMAX_448))
+    g = gpu_search(nv, view, h, S, "wmse", -9, 6, False)
+    o = oracle_search(base, h.cpu().numpy(), S.cpu().numpy(), "wmse", -9, 6, False)
+    assert_same(g, o, "strided")
+
+
+@pytest.mark.parametrize("window", [(-9, 6), (-3, 7), (0, 0), (-1, 0), (0, 5), (-125, 125),
+                                    (-20, 3), (-2, 30)])
+def test_windows(nv, window):
+    lo, hi = window
+    W = _mat(70, 512, torch.bfloat16, seed=11)
+    h = _h(512, seed=12)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    for obj in ("wmse", "mse"):
+        g = gpu_search(nv, W, h if obj == "wmse" else None, S, obj, lo, hi, False)
+        o = oracle_search(W, h.cpu().numpy() if obj == "wmse" else None, S.item(), obj, lo, hi,
+                          False)
+        assert_same(g, o, f"{obj} {window}")
+
+
+def test_edge_groups(nv):
+    """Zero groups, signed zeros, single non-zero, equal magnitudes, clipping at code 126,
+    subnormal base codes, h zeros and extreme h."""
+    out, inp = 64, 256
+    W = _mat(out, inp, torch.float32, seed=21)
+    W[0, :16] = 0.0
+    W[1, :16] = -0.0
+    W[2, :16] = 0.0
+    W[2, 5] = -0.3
+    W[3, :16] = 0.0125
+    W[3, ::3] *= -1
+    W[4, 16:32] = torch.linspace(-2.0, 2.0, 16, device=DEV)     # largest groups -> code 126
+    W[5, :] *= 1e-4                                              # tiny groups -> low codes
+    W[6, :] *= 3e-7                                              # subnormal base codes
+    h = _h(inp, seed=22, spread=6.0)
+    h[::7] = 0.0
+    S = torch.tensor([2.0 / 448 / 6 * 0.7], device=DEV)         # top groups clip at 126
+    for obj, lo, hi, exh in (("wmse", -9, 6, False), ("mse", -3, 7, False), ("wmse", 0, 0, True),
+                             ("mse", 0, 0, True), ("wmse", -8, 7, False)):
+        g = gpu_search(nv, W, h if obj == "wmse" else None, S, obj, lo, hi, exh)
+        o = oracle_search(W, h.cpu().numpy() if obj == "wmse" else None, S.item(), obj, lo, hi,
+                          exh)
+        assert_same(g, o, f"edges {obj} [{lo},{hi}] exh={exh}")
+    assert g["scales"][0, 0, 0] == 0 and g["scales"][0, 1, 0] == 0
+    nib = oracle.unpack_nibbles(g["packed"][0])
+    assert (nib[1, :16] == 8).all() and (nib[0, :16] == 0).all()
+    base = gpu_search(nv, W, None, S, "mse", 0, 0, False)["scales"][0]
+    assert base[4, 1] == 126 and base[6].max() == 1
+
+
+def test_tiny_global_scale_subnormal_codes(nv):
+    """A global scale so small that the lowest codes' effective scales are subnormal binary32
+    values (their reciprocals still finite), with h large enough that losses do not flush."""
+    W = _mat(32, 128, torch.float32, seed=31) * 1e-33
+    h = _h(128, seed=32) * 1e30
+    S = torch.tensor([float(np.float32(2.6e-36))], device=DEV)
+    eff, _ = oracle.scale_tables(S.item())
+    assert eff[1] < np.finfo(np.float32).tiny            # subnormal effective scale
+    for obj, lo, hi, exh in (("wmse", -9, 6, False), ("wmse", 0, 0, True), ("mse", 0, 0, True)):
+        g = gpu_search(nv, W, h if obj == "wmse" else None, S, obj, lo, hi, exh)
+        o = oracle_search(W, h.cpu().numpy() if obj == "wmse" else None, S.item(), obj, lo, hi,
+                          exh)
+        assert_same(g, o, f"tiny S {obj} exh={exh}")
+
+
+def test_pack_parity_and_window_zero(nv):
+    W = _mat(96, 384, torch.bfloat16, seed=41)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(42)
+    scales = torch.randint(0, 127, (96, 24), generator=g, device=DEV, dtype=torch.int32).to(torch.uint8)
+    p = nv.pack(W, scales, S)
+    po = oracle.pack(host_w(W), scales.cpu().numpy(), S.item())
+    np.testing.assert_array_equal(p.cpu().numpy(), po)
+    r = nv.scale_search(W, None, S, nv.MSE, 0, 0)
+    np.testing.assert_array_equal(nv.pack(W, r["scales"], S).cpu().numpy(),
+                                  r["packed"].cpu().numpy())
+
+
+def test_repeatable(nv):
+    W = _mat(512, 1024, torch.bfloat16, seed=51)
+    h = _h(1024, seed=52)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    a = nv.scale_search(W, h, S, nv.WMSE, -9, 6)
+    b = nv.scale_search(W, h, S, nv.WMSE, -9, 6)
+    for k in a:
+        assert torch.equal(a[k], b[k])
+    X = workloads.activations(1000, torch.ones(1024, device=DEV), seed=53, device=DEV)
+    h1 = nv.diag_hessian(X)[0]
+    h2 = nv.diag_hessian(X)[0]
+    assert torch.equal(h1, h2)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("T,inp", [(1, 8), (127, 24), (128, 512), (1000, 520), (3000, 4096)])
+def test_hessian(nv, dtype, T, inp):
+    sig = workloads.channel_sigma(inp, 1.5, seed=inp, device=DEV)
+    X = workloads.activations(T, sig, seed=T, device=DEV, dtype=dtype)
+    acc, h = nv.diag_hessian(X)
+    acc_o, h_o = oracle.diag_hessian(host_w(X))
+    np.testing.assert_allclose(acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+
+
+def test_hessian_padded_and_chunked(nv):
+    full = workloads.activations(2500, torch.ones(640, device=DEV), seed=61, device=DEV)
+    big = torch.zeros((2500, 704), dtype=torch.bfloat16, device=DEV)
+    big[:, :640] = full
+    X = big[:, :640]
+    acc = None
+    acc_o = None
+    for t0 in range(0, 2500, 700):
+        acc, h = nv.diag_hessian(X[t0:t0 + 700], acc, accumulate=acc is not None)
+        acc_o, h_o = oracle.diag_hessian(host_w(full[t0:t0 + 700]), acc_o)
+    np.testing.assert_allclose(acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    # empty token chunk keeps / clears the accumulator
+    acc2, h2 = nv.diag_hessian(X[:0], acc.clone(), accumulate=True)
+    assert torch.equal(acc2, acc)
+    acc3, h3 = nv.diag_hessian(X[:0], acc.clone(), accumulate=False)
+    assert (acc3 == 0).all() and (h3 == 0).all()
+
+
+def test_hessian_batched_segments(nv):
+    counts = np.array([300, 0, 1, 129, 1000, 0, 77, 128], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)])
+    T, inp = int(offs[-1]), 264
+    sig = workloads.channel_sigma(inp, 1.0, seed=71, device=DEV)
+    X = workloads.activations(T, sig, seed=72, device=DEV)
+    seg = torch.from_numpy(offs).to(DEV)
+    acc, h = nv.diag_hessian_batched(X, seg)
+    Xn = host_w(X)
+    for e in range(len(counts)):
+        a_o, h_o = oracle.diag_hessian(Xn[offs[e]:offs[e + 1]])
+        np.testing.assert_allclose(acc[e].cpu().numpy(), a_o, rtol=1e-12, atol=0)
+        np.testing.assert_allclose(h[e].cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    acc2, _ = nv.diag_hessian_batched(X, seg, acc.clone(), accumulate=True)
+    np.testing.assert_allclose(acc2.cpu().numpy(), 2 * acc.cpu().numpy(), rtol=1e-12)
+
+
+def test_global_scale_rules_and_batch(nv):
+    W = _mat(33, 96, torch.bfloat16, seed=81, batch=5)
+    W[3] = 0
+    for rule, orule in ((nv.GS_AMAX_448, oracle.GS_AMAX_448), (nv.GS_AMAX_256, oracle.GS_AMAX_256)):
+        S = nv.global_scale(W, rule).cpu().numpy()
+        for b in range(5):
+            assert S[b] == np.float32(oracle.global_scale(host_w(W[b]), orule))
+    assert S[3] == 1.0
+
+
+def test_empty_inputs(nv):
+    W = torch.empty((0, 64), dtype=torch.bfloat16, device=DEV)
+    S = nv.global_scale(W)
+    assert S.item() == 1.0
+    r = nv.scale_search(W, torch.ones(64, device=DEV), S, nv.WMSE)
+    assert r["scales"].numel() == 0
