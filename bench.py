@@ -1,0 +1,315 @@
+"""Benchmark of the NVFP4 block-scale search hot path on one MI355X.
+
+One step = the whole path over one synthetic layer held in HBM:
+  diagonal Hessian over X -> global scale of W -> scale search + pack for every mode the
+  workload names (attn8b: MSE [-3,7] and WMSE [-8,7]).
+Prints one JSON line. `value` is weight-searches per second: every mode run searches each of the
+layer's weights once, so a step counts n_weights * n_modes. Several input sets are rotated
+(more bytes than the 256 MB MALL) so that every step reads its inputs from HBM.
+
+Per-kernel times come from HIP events recorded on the launch stream around each library call
+inside the timed steps. The dominant kernel's roofline entry uses algorithmic bytes / flops
+per launch; `traffic` is read from the committed rocprofv3 counter summary when
+its kernel-source hash matches the current sources, else null.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload attn8b] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+# fp32 VALU peak of the build: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz = 39.3e12 lane-ops/s,
+# x 2 flops per fma = 78.6 TFLOP/s. (The published 157.3 TFLOP/s counts packed dual-fp32 FMAs,
+# which this build does not emit.)
+VALU_PEAK_TFLOPS = 78.6
+VALU_PUBLISHED_TFLOPS = 157.3
+# algorithmic flops per element and candidate: |w|*r (1), E2M1 rounding (1), residual fma (2),
+# accumulate fma (2), and for WMSE the h*d weighting (1)
+FLOPS_PER_ELEM_CAND = {"wmse": 7, "mse": 6}
+
+METRIC = "weights/s and HBM GB/s (fraction of peak) for scale search+pack; h-reduce GB/s"
+KERNEL_SOURCES = ["block_scale_search_amd/csrc/scale_search.hip",
+                  "block_scale_search_amd/csrc/device_formats.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def n_candidates(mode) -> int:
+    return 126 if mode.exhaustive else mode.hi - mode.lo + 1
+
+
+class Layer:
+    """One input set of a workload, resident on the GPU, plus its output buffers."""
+
+    def __init__(self, cfg, k: int, dev):
+        import torch
+
+        from block_scale_search_amd import workloads
+        cfg_k = type(cfg)(**{**cfg.__dict__, "seed": cfg.seed + 100 * k})
+        self.W = workloads.make_weights(cfg_k, dev)
+        sigma = workloads.make_sigma(cfg_k, dev)
+        self.chunks, self.seg = [], None
+        for c in range(workloads.n_chunks(cfg)):
+            X, offs = workloads.make_activation_chunk(cfg_k, sigma, c, dev)
+            self.chunks.append(X)
+            if offs is not None:
+                self.seg = torch.from_numpy(offs).to(dev)
+        self.batch = cfg.batch
+        n = cfg.inp
+        E = cfg.batch
+        self.h_acc = torch.zeros((E, n) if E > 1 else (n,), dtype=torch.float64, device=dev)
+        self.h = torch.empty((E, n) if E > 1 else (n,), dtype=torch.float32, device=dev)
+        self.S = torch.empty(E, dtype=torch.float32, device=dev)
+        G = cfg.batch * cfg.out * (n // 16)
+        self.scales = [torch.empty(G, dtype=torch.uint8, device=dev) for _ in cfg.modes]
+        self.packed = [torch.empty(G * 8, dtype=torch.uint8, device=dev) for _ in cfg.modes]
+
+
+class Runner:
+    def __init__(self, cfg, n_sets: int, dev):
+        import torch
+
+        from block_scale_search_amd import nvfp4
+        self.nv, self.cfg, self.dev = nvfp4, cfg, dev
+        self.sets = [Layer(cfg, k, dev) for k in range(n_sets)]
+        T = cfg.chunk_tokens or cfg.tokens
+        E = cfg.batch
+        self.ws_h = torch.zeros(max(1, nvfp4.nvfp4_diag_hessian_workspace_size(T, cfg.inp, E)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_s = torch.zeros(max(1, nvfp4.nvfp4_global_scale_workspace_size(E, cfg.out, cfg.inp)),
+                                dtype=torch.uint8, device=dev)
+        self.rule = nvfp4.GS_AMAX_256 if cfg.gs_rule == "amax256" else nvfp4.GS_AMAX_448
+
+    def calls(self, s: Layer):
+        """The step as a list of (label, call) pairs in stream order; each call is a prepared
+        C-ABI invocation (arguments marshalled once) on the current stream."""
+        nv, cfg = self.nv, self.cfg
+        b, o, n = cfg.batch, cfg.out, cfg.inp
+        ldw, sw = n, o * n
+        out = []
+        for ci, X in enumerate(s.chunks):
+            T = X.shape[0]
+            if s.seg is not None:
+                out.append(("h_reduce", nv.nvfp4_diag_hessian_batched(
+                    X, s.seg, b, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, prepare=True)))
+            else:
+                out.append(("h_reduce", nv.nvfp4_diag_hessian(
+                    X, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, prepare=True)))
+        out.append(("global_scale", nv.nvfp4_global_scale(
+            s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True)))
+        for mi, m in enumerate(cfg.modes):
+            wm = m.objective == "wmse"
+            out.append((f"search:{m.label}", nv.nvfp4_scale_search(
+                s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
+                nv.WMSE if wm else nv.MSE, m.lo, m.hi, m.exhaustive, s.S, s.scales[mi],
+                s.packed[mi], prepare=True)))
+        return out
+
+
+def algorithmic(cfg, label: str):
+    """(bytes, flops) one call moves / computes by the method's definition."""
+    n_w = cfg.n_weights
+    wb = 2 if str(cfg.w_dtype).endswith("bfloat16") else 4
+    if label == "h_reduce":
+        T = cfg.chunk_tokens or cfg.tokens
+        return T * cfg.inp * 2 + cfg.batch * cfg.inp * 12, 2 * T * cfg.inp
+    if label == "global_scale":
+        return n_w * wb + 4 * cfg.batch, n_w
+    mode = next(m for m in cfg.modes if label == f"search:{m.label}")
+    bytes_ = n_w * wb + n_w // 2 + n_w // 16 + (cfg.batch * cfg.inp * 4 if mode.objective == "wmse" else 0)
+    flops = n_w * n_candidates(mode) * FLOPS_PER_ELEM_CAND[mode.objective]
+    return bytes_, flops
+
+
+def cpu_baseline(cfg, threads: int):
+    """The oracle, as it stands, over the same workload's first input set (host cores)."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from block_scale_search_amd import workloads
+
+    def bits(t):
+        t = t.cpu()
+        return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
+
+    W = bits(workloads.make_weights(cfg, "cpu"))
+    sigma = workloads.make_sigma(cfg, "cpu")
+    Xs = [bits(workloads.make_activation_chunk(cfg, sigma, c, "cpu")[0])
+          for c in range(workloads.n_chunks(cfg))]
+    rows = W.shape[-2]
+    if cfg.batch > 1 or rows * cfg.inp > (1 << 26):
+        raise SystemExit("cpu baseline is sized for single-matrix workloads up to 64M weights")
+    t0 = time.perf_counter()
+    acc = None
+    for X in Xs:
+        acc, h = oracle.diag_hessian(X, acc, threads=threads)
+    S = oracle.global_scale(W, oracle.GS_AMAX_256 if cfg.gs_rule == "amax256" else oracle.GS_AMAX_448)
+    for m in cfg.modes:
+        oracle.scale_search(W, h if m.objective == "wmse" else None,
+                            oracle.WMSE if m.objective == "wmse" else oracle.MSE, m.lo, m.hi,
+                            m.exhaustive, S, threads=threads)
+    dt = time.perf_counter() - t0
+    searched = cfg.n_weights * len(cfg.modes)
+    return {"value": searched / dt, "unit": "weights/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {cfg.name} workload once (first input set): h over "
+                      f"{cfg.tokens}x{cfg.inp} tokens, global scale, "
+                      f"{' + '.join(m.label for m in cfg.modes)} over {cfg.out}x{cfg.inp} "
+                      f"weights; {dt:.2f} s wall on {threads} threads"}
+
+
+def read_traffic(workload: str, kernel_label: str):
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("per_launch_bytes", {}).get(kernel_label)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="attn8b")
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = enough for >1 GB)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="run one 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU split is "
+              "described in DESIGN.md and is not launched.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from block_scale_search_amd import workloads
+    cfg = workloads.CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    per_set = cfg.n_weights * (2 if str(cfg.w_dtype).endswith("bfloat16") else 4) + \
+        cfg.tokens * cfg.inp * 2
+    n_sets = args.sets or max(1, min(8, -(-(1 << 30) // per_set)))
+    print(f"# workload {cfg.name}: {cfg.description}; {n_sets} input set(s)", file=sys.stderr,
+          flush=True)
+    runner = Runner(cfg, n_sets, dev)
+    torch.cuda.synchronize()
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    steps = [runner.calls(s) for s in runner.sets]
+    for i in range(args.warmup):
+        for _, f in steps[i % n_sets]:
+            f()
+    torch.cuda.synchronize()
+
+    labels = [lab for lab, _ in steps[0]]
+    ev = []
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(args.steps):
+        row = []
+        for _, f in steps[i % n_sets]:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            row.append((e0, e1))
+        ev.append(row)
+    t_end.record()
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    per_label = {}
+    for row in ev:
+        for lab, (e0, e1) in zip(labels, row):
+            per_label.setdefault(lab, []).append(e0.elapsed_time(e1) * 1e3)  # us
+    kernels = {}
+    for lab, us in per_label.items():
+        us_avg = sum(us) / len(us)
+        nb, nf = algorithmic(cfg, lab)
+        k = {"avg_us": round(us_avg, 3), "calls_per_step": labels.count(lab),
+             "alg_bytes": nb, "GB/s": round(nb / us_avg / 1e3, 1),
+             "frac_hbm": round(nb / us_avg / 1e3 / HBM_PEAK_GBS, 4)}
+        if lab.startswith("search"):
+            k["weights/s"] = cfg.n_weights / (us_avg * 1e-6)
+            k["TFLOP/s"] = round(nf / us_avg / 1e6, 2)
+            k["frac_valu_78.6"] = round(nf / us_avg / 1e6 / VALU_PEAK_TFLOPS, 4)
+        kernels[lab] = k
+    dom = max((l for l in kernels if l.startswith("search")),
+              key=lambda l: kernels[l]["avg_us"] * kernels[l]["calls_per_step"])
+    nb, nf = algorithmic(cfg, dom)
+    us_dom = kernels[dom]["avg_us"]
+    achieved = nf / us_dom / 1e6
+    roofline = {"bound": "alu", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / VALU_PEAK_TFLOPS, 4),
+                "frac_of_published_157.3": round(achieved / VALU_PUBLISHED_TFLOPS, 4),
+                "traffic": read_traffic(cfg.name, dom),
+                "alg_bytes_per_launch": nb, "alg_flops_per_launch": nf,
+                "hbm_GB/s_algorithmic": kernels[dom]["GB/s"],
+                "hbm_frac_algorithmic": kernels[dom]["frac_hbm"]}
+
+    cpu = None
+    if not args.no_cpu:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        try:
+            cpu = cpu_baseline(cfg, threads)
+        except SystemExit as e:
+            cpu = {"value": None, "unit": "weights/s", "cores": 0, "kind": "oracle",
+                   "sample": str(e)}
+
+    searched = cfg.n_weights * len(cfg.modes)
+    line = {
+        "metric": METRIC,
+        "value": searched / (ms_per_step * 1e-3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; stands in for the pages' calibration sets and checkpoints)",
+        "config": {"workload": cfg.description, "name": cfg.name,
+                   "modes": [m.label for m in cfg.modes], "global_scale": cfg.gs_rule,
+                   "weights_per_step": searched, "input_sets_rotated": n_sets},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "h_reduce_GB/s": kernels["h_reduce"]["GB/s"],
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

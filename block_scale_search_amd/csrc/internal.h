@@ -9,7 +9,7 @@
 namespace nvfp4 {
 
 // Diagonal Hessian: rows per partial tile and the tile count bound used for workspace sizing.
-constexpr int kHessRowsPerTile = 128;
+constexpr int kHessRowsPerTile = 512;
 constexpr int kHessWaves = 16;
 int64_t hessian_max_tiles(int64_t tokens, int64_t segments);
 size_t hessian_workspace_bytes(int64_t tokens, int64_t in, int64_t segments);

@@ -306,10 +306,40 @@ __global__ __launch_bounds__(kSearchThreads) void k_pack(
     reinterpret_cast<uint2*>(packed)[gidx] = make_uint2(p0, p1);
 }
 
-// Global scale, pass 1: max |w| of a slice of rows per workgroup, as the binary32 bit pattern
-// of a non-negative value (ordered like unsigned integers). Exact, order-free.
+// Global scale: S = amax / 2688 (448 * 6) or amax / 1536 (256 * 6), S = 1 if amax = 0.
+// max |w| is taken on binary32 bit patterns of non-negative values (ordered like unsigned
+// integers): exact and independent of order. Pass 1: each workgroup reduces its share (8 loads
+// of 16 B in flight per lane) to one partial. Pass 2: one workgroup per matrix reduces the
+// partials and writes S.
 constexpr int kAmaxThreads = 256;
-constexpr int kAmaxBlocksPerMatrix = 256;
+constexpr int kAmaxLoads = 8;
+constexpr int kAmaxMaxBlocks = 1024;
+
+template <bool BF16>
+__device__ __forceinline__ uint32_t absmax_bits(const uint4 d) {
+    if constexpr (BF16) {
+        const uint32_t x[4] = {d.x & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu,
+                               d.w & 0x7FFF7FFFu};
+        uint32_t m = 0u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m = max(m, max(x[i] << 16, x[i] & 0xFFFF0000u));
+        return m;
+    } else {
+        return max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu),
+                   max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu));
+    }
+}
+
+__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* wmax) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t r = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kAmaxThreads / 64; ++i) r = max(r, wmax[i]);
+    return r;
+}
 
 template <bool BF16>
 __global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const uint8_t* __restrict__ W,
@@ -318,59 +348,51 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const uint8_t* __
                                                                int64_t stride_w_bytes,
                                                                uint32_t* __restrict__ partial) {
     constexpr int C = BF16 ? 8 : 4;  // elements per 16-byte load
+    __shared__ uint32_t wmax[kAmaxThreads / 64];
     const int64_t batch = blockIdx.y;
     const uint8_t* base = W + batch * stride_w_bytes;
-    const int64_t vpr = in / C;  // 16-byte loads per row (in % 16 == 0)
-    // A dense matrix is one long row; otherwise rows are visited one by one.
+    const int64_t vpr = in / C;
     const bool dense = ldw_bytes == vpr * 16;
-    const int64_t rows = dense ? 1 : out;
-    const int64_t row_vec = dense ? out * vpr : vpr;
-    uint32_t m = 0u;
-    const int64_t gtid = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+    const int64_t nvec = out * vpr;
     const int64_t gsize = (int64_t)gridDim.x * kAmaxThreads;
-    for (int64_t r = 0; r < rows; ++r) {
-        const uint4* rp = reinterpret_cast<const uint4*>(base + r * ldw_bytes);
-        for (int64_t k = gtid; k < row_vec; k += gsize) {
-            const uint4 d = rp[k];
-            if constexpr (BF16) {
-                const uint32_t x[4] = {d.x & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu,
-                                       d.w & 0x7FFF7FFFu};
+    uint32_t m = 0u;
+    for (int64_t v0 = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; v0 < nvec;
+         v0 += kAmaxLoads * gsize) {
+        uint4 d[kAmaxLoads];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) m = max(m, max(x[i] << 16, x[i] & 0xFFFF0000u));
-            } else {
-                m = max(m, max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu),
-                               max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu)));
+        for (int k = 0; k < kAmaxLoads; ++k) {
+            const int64_t v = v0 + k * gsize;
+            d[k] = make_uint4(0u, 0u, 0u, 0u);
+            if (v < nvec) {
+                const int64_t off = dense ? v * 16 : (v / vpr) * ldw_bytes + (v % vpr) * 16;
+                d[k] = *reinterpret_cast<const uint4*>(base + off);
             }
         }
-    }
-    // wave reduction, then across the workgroup's waves
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    __shared__ uint32_t wmax[kAmaxThreads / 64];
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        uint32_t r = wmax[0];
-        for (int i = 1; i < kAmaxThreads / 64; ++i) r = max(r, wmax[i]);
-        partial[batch * gridDim.x + blockIdx.x] = r;
+        for (int k = 0; k < kAmaxLoads; ++k) m = max(m, absmax_bits<BF16>(d[k]));
     }
+    m = block_max(m, wmax);
+    if (threadIdx.x == 0) partial[batch * gridDim.x + blockIdx.x] = m;
 }
 
-// Global scale, pass 2: S = amax / 2688 (448 * 6) or amax / 1536 (256 * 6); 1 if amax = 0.
-__global__ void k_global_scale_finalize(const uint32_t* __restrict__ partial, int64_t nblk,
-                                        int64_t batch, int rule, float* __restrict__ S) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= batch) return;
-    uint32_t m = 0u;
-    for (int64_t i = 0; i < nblk; ++i) m = max(m, partial[b * nblk + i]);
-    const float amax = __uint_as_float(m);
-    S[b] = amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
+__global__ __launch_bounds__(kAmaxThreads) void k_global_scale_finalize(
+    const uint32_t* __restrict__ partial, int64_t nblk, int rule, float* __restrict__ S) {
+    __shared__ uint32_t wmax[kAmaxThreads / 64];
+    const int64_t batch = blockIdx.x;
+    uint32_t r = 0u;
+    for (int64_t i = threadIdx.x; i < nblk; i += kAmaxThreads)
+        r = max(r, partial[batch * nblk + i]);
+    r = block_max(r, wmax);
+    if (threadIdx.x == 0) {
+        const float amax = __uint_as_float(r);
+        S[batch] = amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
+    }
 }
 
 int64_t amax_blocks(int64_t out, int64_t in) {
-    const int64_t vec = out * (in / 4);
-    const int64_t want = (vec + kAmaxThreads * 16 - 1) / (kAmaxThreads * 16);
-    return want < 1 ? 1 : (want > kAmaxBlocksPerMatrix ? kAmaxBlocksPerMatrix : want);
+    const int64_t vec = out * (in / 4);  // upper bound on 16-byte loads (f32)
+    const int64_t want = (vec + kAmaxThreads * kAmaxLoads - 1) / (kAmaxThreads * kAmaxLoads);
+    return want < 1 ? 1 : (want > kAmaxMaxBlocks ? kAmaxMaxBlocks : want);
 }
 
 }  // namespace
@@ -394,8 +416,8 @@ hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t 
         hipLaunchKernelGGL(k_amax_partial<false>, grid, dim3(kAmaxThreads), 0, stream,
                            static_cast<const uint8_t*>(W), out, in, ldw * esz, stride_w * esz,
                            partial);
-    hipLaunchKernelGGL(k_global_scale_finalize, dim3((uint32_t)((batch + 63) / 64)), dim3(64), 0,
-                       stream, partial, nblk, batch, rule, S);
+    hipLaunchKernelGGL(k_global_scale_finalize, dim3((uint32_t)batch), dim3(kAmaxThreads), 0,
+                       stream, partial, nblk, rule, S);
     return hipGetLastError();
 }
 

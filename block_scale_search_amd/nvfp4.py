@@ -8,7 +8,7 @@ there is no CPU path. Importing this module fails if the library has not been bu
 (``python -m block_scale_search_amd.build``).
 
 The convenience wrappers at the end (``diag_hessian``, ``global_scale``, ``scale_search``,
-``pack``) allocate outputs and workspaces with torch and call the entry points.
+``pack``) allocate outputs and (zero-filled) workspaces with torch and call the entry points.
 """
 from __future__ import annotations
 
@@ -60,6 +60,20 @@ def _check(status: int, where: str) -> None:
         raise Nvfp4Error(status, where)
 
 
+def _run(fname: str, args: tuple, prepare: bool):
+    """Call C entry point `fname` with marshalled `args`, or (prepare=True) return a
+    zero-argument callable that makes exactly that call; the tensors behind the pointers must
+    then stay alive and unchanged in size while the callable is used."""
+    f = getattr(_lib, fname)
+    if not prepare:
+        _check(f(*args), fname)
+        return None
+
+    def call():
+        _check(f(*args), fname)
+    return call
+
+
 def _dev(t: torch.Tensor | None, name: str, dtypes=None):
     if t is None:
         return None
@@ -104,40 +118,40 @@ def nvfp4_global_scale_workspace_size(batch: int, out: int, inp: int) -> int:
     return int(_lib.nvfp4_global_scale_workspace_size(batch, out, inp))
 
 
-def nvfp4_diag_hessian(X, tokens, inp, ldx, h_acc, h, accumulate, workspace, stream=None):
+def nvfp4_diag_hessian(X, tokens, inp, ldx, h_acc, h, accumulate, workspace, stream=None, prepare=False):
     _need(h_acc, inp, "h_acc")
     if h is not None:
         _need(h, inp, "h")
-    _check(_lib.nvfp4_diag_hessian(
+    return _run("nvfp4_diag_hessian", (
         _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx,
         _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)), "nvfp4_diag_hessian")
+        _stream(stream)), prepare)
 
 
 def nvfp4_diag_hessian_batched(X, seg_offsets, segments, total_tokens, inp, ldx, h_acc, h,
-                               accumulate, workspace, stream=None):
+                               accumulate, workspace, stream=None, prepare=False):
     _need(h_acc, segments * inp, "h_acc")
     if h is not None:
         _need(h, segments * inp, "h")
-    _check(_lib.nvfp4_diag_hessian_batched(
+    return _run("nvfp4_diag_hessian_batched", (
         _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X),
         _dev(seg_offsets, "seg_offsets", (torch.int64,)), segments, total_tokens, inp, ldx,
         _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
-        _stream(stream)), "nvfp4_diag_hessian_batched")
+        _stream(stream)), prepare)
 
 
-def nvfp4_global_scale(W, batch, out, inp, ldw, stride_w, rule, S, workspace, stream=None):
+def nvfp4_global_scale(W, batch, out, inp, ldw, stride_w, rule, S, workspace, stream=None, prepare=False):
     _need(S, batch, "S")
-    _check(_lib.nvfp4_global_scale(
+    return _run("nvfp4_global_scale", (
         _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
         rule, _dev(S, "S", (torch.float32,)), _dev(workspace, "workspace"),
-        workspace.numel() * workspace.element_size(), _stream(stream)), "nvfp4_global_scale")
+        workspace.numel() * workspace.element_size(), _stream(stream)), prepare)
 
 
 def nvfp4_scale_search(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h, objective,
-                       lo, hi, exhaustive, S, scales, packed, loss=None, offset=None, stream=None):
+                       lo, hi, exhaustive, S, scales, packed, loss=None, offset=None, stream=None, prepare=False):
     G = batch * out * (inp // 16)
     _need(scales, G, "scales")
     _need(packed, G * 8, "packed")
@@ -146,22 +160,22 @@ def nvfp4_scale_search(W, batch, out, inp, ldw, stride_w, group_size, h, stride_
         _need(loss, G, "loss")
     if offset is not None:
         _need(offset, G, "offset")
-    _check(_lib.nvfp4_scale_search(
+    return _run("nvfp4_scale_search", (
         _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
         group_size, _dev(h, "h", (torch.float32,)), stride_h, objective, lo, hi, int(exhaustive),
         _dev(S, "S", (torch.float32,)), _dev(scales, "scales", (torch.uint8,)),
         _dev(packed, "packed", (torch.uint8,)), _dev(loss, "loss", (torch.float32,)),
-        _dev(offset, "offset", (torch.int8,)), _stream(stream)), "nvfp4_scale_search")
+        _dev(offset, "offset", (torch.int8,)), _stream(stream)), prepare)
 
 
-def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None):
+def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None, prepare=False):
     G = batch * out * (inp // 16)
     _need(scales, G, "scales")
     _need(packed, G * 8, "packed")
-    _check(_lib.nvfp4_pack(
+    return _run("nvfp4_pack", (
         _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
         _dev(scales, "scales", (torch.uint8,)), _dev(S, "S", (torch.float32,)),
-        _dev(packed, "packed", (torch.uint8,)), _stream(stream)), "nvfp4_pack")
+        _dev(packed, "packed", (torch.uint8,)), _stream(stream)), prepare)
 
 
 # --- convenience wrappers (allocate outputs with torch, then call the entry points) ----------
@@ -188,7 +202,7 @@ def diag_hessian(X: torch.Tensor, h_acc: torch.Tensor | None = None, accumulate:
     if h_acc is None:
         h_acc = torch.zeros(n, dtype=torch.float64, device=X.device)
     h = torch.empty(n, dtype=torch.float32, device=X.device)
-    ws = torch.empty(max(1, nvfp4_diag_hessian_workspace_size(T, n, 1)), dtype=torch.uint8,
+    ws = torch.zeros(max(1, nvfp4_diag_hessian_workspace_size(T, n, 1)), dtype=torch.uint8,
                      device=X.device)
     nvfp4_diag_hessian(X, T, n, X.stride(0), h_acc, h, accumulate, ws, stream)
     return h_acc, h
@@ -202,7 +216,7 @@ def diag_hessian_batched(X: torch.Tensor, seg_offsets: torch.Tensor,
     if h_acc is None:
         h_acc = torch.zeros((E, n), dtype=torch.float64, device=X.device)
     h = torch.empty((E, n), dtype=torch.float32, device=X.device)
-    ws = torch.empty(max(1, nvfp4_diag_hessian_workspace_size(T, n, E)), dtype=torch.uint8,
+    ws = torch.zeros(max(1, nvfp4_diag_hessian_workspace_size(T, n, E)), dtype=torch.uint8,
                      device=X.device)
     nvfp4_diag_hessian_batched(X, seg_offsets, E, T, n, X.stride(0), h_acc, h, accumulate, ws,
                                stream)
@@ -212,7 +226,7 @@ def diag_hessian_batched(X: torch.Tensor, seg_offsets: torch.Tensor,
 def global_scale(W: torch.Tensor, rule: int = GS_AMAX_448, stream=None) -> torch.Tensor:
     b, o, n, ldw, sw = _bmat(W)
     S = torch.empty(b, dtype=torch.float32, device=W.device)
-    ws = torch.empty(max(1, nvfp4_global_scale_workspace_size(b, o, n)), dtype=torch.uint8,
+    ws = torch.zeros(max(1, nvfp4_global_scale_workspace_size(b, o, n)), dtype=torch.uint8,
                      device=W.device)
     nvfp4_global_scale(W, b, o, n, ldw, sw, rule, S, ws, stream)
     return S

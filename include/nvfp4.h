@@ -106,7 +106,8 @@ nvfp4_status nvfp4_diag_hessian_batched(const void* X, int x_dtype, const int64_
  * W        device, `batch` matrices [out, in], row stride ldw, matrix stride stride_w (elements),
  *          bf16 or f32, 16-byte aligned rows.
  * S        device, float [batch]: S[b] from the max |w| of matrix b by `rule`.
- * workspace  device scratch of nvfp4_global_scale_workspace_size(batch, out, in) bytes.
+ * workspace  device scratch of nvfp4_global_scale_workspace_size(batch, out, in) bytes,
+ *          4-byte aligned; its contents are overwritten and need no initialisation.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t out, int64_t in);
 

@@ -102,7 +102,7 @@ def test_pack_and_global_scale_reject_bad_arguments(lib):
 def test_diag_hessian_rejects_bad_arguments(lib):
     from block_scale_search_amd import nvfp4 as n
     ws = lib.nvfp4_diag_hessian_workspace_size(1000, 64, 1)
-    assert ws >= 8 * 8 * 64                                        # ceil(1000/128) tiles of fp64
+    assert ws >= 2 * 8 * 64                                        # ceil(1000/512) tiles of fp64
     assert lib.nvfp4_diag_hessian_workspace_size(-1, 64, 1) == 0
     assert lib.nvfp4_diag_hessian_workspace_size(1000, 64, 4) > ws  # + per-expert tiles
     H = lib.nvfp4_diag_hessian

@@ -221,7 +221,8 @@ def test_repeatable(nv):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
-@pytest.mark.parametrize("T,inp", [(1, 8), (127, 24), (128, 512), (1000, 520), (3000, 4096)])
+@pytest.mark.parametrize("T,inp", [(1, 8), (127, 24), (511, 512), (512, 136), (513, 1000),
+                                   (3000, 4096), (5000, 200)])
 def test_hessian(nv, dtype, T, inp):
     sig = workloads.channel_sigma(inp, 1.5, seed=inp, device=DEV)
     X = workloads.activations(T, sig, seed=T, device=DEV, dtype=dtype)
@@ -265,6 +266,41 @@ def test_hessian_batched_segments(nv):
         np.testing.assert_allclose(h[e].cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
     acc2, _ = nv.diag_hessian_batched(X, seg, acc.clone(), accumulate=True)
     np.testing.assert_allclose(acc2.cpu().numpy(), 2 * acc.cpu().numpy(), rtol=1e-12)
+
+
+def test_workspace_reuse(nv):
+    """One workspace serves a sequence of calls (token counts and element types vary) with no
+    clearing in between: nothing a call leaves behind changes the next result."""
+    n = 520
+    ws = torch.full((nv.nvfp4_diag_hessian_workspace_size(5000, n, 1),), 0xA5, dtype=torch.uint8,
+                     device=DEV)
+    for T, dt in ((3000, torch.bfloat16), (100, torch.float32), (5000, torch.bfloat16),
+                  (0, torch.bfloat16), (513, torch.float32), (3000, torch.bfloat16)):
+        X = workloads.activations(T, torch.ones(n, device=DEV), seed=T + 1, device=DEV, dtype=dt)
+        acc = torch.empty(n, dtype=torch.float64, device=DEV)
+        h = torch.empty(n, dtype=torch.float32, device=DEV)
+        nv.nvfp4_diag_hessian(X, T, n, n, acc, h, False, ws)
+        want = oracle.diag_hessian(host_w(X))[0] if T else np.zeros(n)
+        np.testing.assert_allclose(acc.cpu().numpy(), want, rtol=1e-12)
+    offs = torch.tensor([0, 10, 10, 600, 1700], dtype=torch.int64, device=DEV)
+    wsb = torch.full((nv.nvfp4_diag_hessian_workspace_size(1700, n, 4),), 0xA5, dtype=torch.uint8,
+                      device=DEV)
+    for rep in range(3):
+        X = workloads.activations(1700, torch.ones(n, device=DEV), seed=rep, device=DEV)
+        acc = torch.empty(4 * n, dtype=torch.float64, device=DEV)
+        nv.nvfp4_diag_hessian_batched(X, offs, 4, 1700, n, n, acc, None, False, wsb)
+        Xn = host_w(X)
+        for e in range(4):
+            o0, o1 = int(offs[e]), int(offs[e + 1])
+            want = oracle.diag_hessian(Xn[o0:o1])[0] if o1 > o0 else np.zeros(n)
+            np.testing.assert_allclose(acc[e * n:(e + 1) * n].cpu().numpy(), want, rtol=1e-12)
+    wss = torch.full((nv.nvfp4_global_scale_workspace_size(1, 4096, 4096),), 0xA5, dtype=torch.uint8,
+                      device=DEV)
+    for out, inp, dt in ((512, 4096, torch.bfloat16), (64, 512, torch.float32), (4096, 4096, torch.bfloat16)):
+        W = _mat(out, inp, dt, seed=out + inp)
+        S = torch.empty(1, dtype=torch.float32, device=DEV)
+        nv.nvfp4_global_scale(W, 1, out, inp, inp, out * inp, nv.GS_AMAX_448, S, wss)
+        assert S.item() == np.float32(oracle.global_scale(host_w(W), oracle.GS_AMAX_448))
 
 
 def test_global_scale_rules_and_batch(nv):
