@@ -94,7 +94,7 @@ def _dtype_code(a: np.ndarray) -> int:
 
 
 def default_threads() -> int:
-    return max(1, len(os.sched_getaffinity(0)))
+    return max(1, min(16, len(os.sched_getaffinity(0))))
 
 
 # --- element formats -------------------------------------------------------------------------

@@ -21,3 +21,10 @@ def oracle_mod():
     if not os.path.exists(os.path.join(ROOT, "oracle", "libnvfp4_ref.so")):
         oracle.build()
     return oracle
+
+
+@pytest.fixture(scope="module")
+def nv():
+    """The GPU library's binding (imports only when a GPU test asks for it)."""
+    from block_scale_search_amd import nvfp4
+    return nvfp4

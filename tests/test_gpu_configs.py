@@ -1,0 +1,144 @@
+"""GPU parity at the full workload sizes, in the launch configuration bench.py uses.
+
+For each synthetic layer (8B attention, 8B MLP down, 128-expert MoE batch, both 70B MLP shapes):
+  - h from the GPU against the oracle's h on every column (1e-5 relative; binary64 sums 1e-12);
+  - the global scale S against the oracle's, exactly;
+  - every mode of the workload on the whole matrix on the GPU, compared bit for bit with the
+    oracle on sampled rows (first, last and random rows; for the MoE batch, rows of several
+    experts), using the same h;
+  - the flip fraction: groups whose scale changes when the search uses the GPU's own h instead
+    of the oracle's (must stay below 1e-4), printed for the record.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_scale_search_amd import workloads
+from gpu_helpers import DEV, OBJ, assert_same, host_w
+
+pytestmark = pytest.mark.gpu
+
+FLIP_MAX = 1e-4
+
+
+def _rows(out, n, seed):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, 1, out - 1], rng.choice(out, n, replace=False)]))
+
+
+def _host_h(X_chunks, seg=None, E=1):
+    """Oracle h (binary64 running sum and binary32) from the GPU's X, chunk by chunk."""
+    acc = None
+    if seg is None:
+        for X in X_chunks:
+            acc, h = oracle.diag_hessian(host_w(X), acc)
+        return acc, h
+    Xn = host_w(X_chunks[0])
+    accs, hs = [], []
+    for e in range(E):
+        a, h = oracle.diag_hessian(Xn[seg[e]:seg[e + 1]])
+        accs.append(a)
+        hs.append(h)
+    return np.stack(accs), np.stack(hs)
+
+
+def _gpu_h(nv, X_chunks, seg_t=None):
+    acc = None
+    h = None
+    for ci, X in enumerate(X_chunks):
+        if seg_t is not None:
+            acc, h = nv.diag_hessian_batched(X, seg_t)
+        else:
+            acc, h = nv.diag_hessian(X, acc, accumulate=ci > 0)
+    return acc, h
+
+
+def _run_config(nv, name, sample_rows=40):
+    cfg = workloads.CONFIGS[name]
+    print(f"\n[{name}] {cfg.description}", flush=True)
+    W = workloads.make_weights(cfg, DEV)
+    sigma = workloads.make_sigma(cfg, DEV)
+    chunks, seg = [], None
+    for c in range(workloads.n_chunks(cfg)):
+        X, offs = workloads.make_activation_chunk(cfg, sigma, c, DEV)
+        chunks.append(X)
+        seg = offs
+    seg_t = torch.from_numpy(seg).to(DEV) if seg is not None else None
+    acc_g, h_g = _gpu_h(nv, chunks, seg_t)
+    torch.cuda.synchronize()
+    acc_o, h_o = _host_h(chunks, seg, cfg.batch)
+    np.testing.assert_allclose(acc_g.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h_g.cpu().numpy(), h_o, rtol=1e-5, atol=0)
+    n_h_diff = int((h_g.cpu().numpy() != h_o).sum())
+    print(f"[{name}] h: {h_o.size} columns, {n_h_diff} differ in the last binary32 bit", flush=True)
+    del chunks
+
+    rule = nv.GS_AMAX_256 if cfg.gs_rule == "amax256" else nv.GS_AMAX_448
+    orule = oracle.GS_AMAX_256 if cfg.gs_rule == "amax256" else oracle.GS_AMAX_448
+    S = nv.global_scale(W, rule)
+    S_h = S.cpu().numpy().reshape(-1)
+    Wb = W if W.dim() == 3 else W[None]
+    for b in range(cfg.batch):
+        assert S_h[b] == np.float32(oracle.global_scale(host_w(Wb[b]), orule)), f"S[{b}]"
+
+    h_oracle_dev = torch.from_numpy(np.ascontiguousarray(h_o)).to(DEV)
+    for mode in cfg.modes:
+        wm = mode.objective == "wmse"
+        obj = nv.WMSE if wm else nv.MSE
+        g = nv.scale_search(W, h_g if wm else None, S, obj, mode.lo, mode.hi, mode.exhaustive)
+        torch.cuda.synchronize()
+        # sampled rows against the oracle with the identical h
+        if cfg.batch == 1:
+            rows = _rows(cfg.out, sample_rows, seed=cfg.seed)
+            picks = [(0, rows)]
+        else:
+            rng = np.random.default_rng(cfg.seed)
+            picks = [(int(e), _rows(cfg.out, 4, seed=int(e)))
+                     for e in np.unique(np.concatenate([[0, cfg.batch - 1],
+                                                        rng.choice(cfg.batch, 6, replace=False)]))]
+        hg = h_g.cpu().numpy().reshape(cfg.batch, -1)
+        for b, rows in picks:
+            Wr = host_w(Wb[b][torch.from_numpy(rows).to(DEV)])
+            o = oracle.scale_search(Wr, hg[b] if wm else None, OBJ[mode.objective], mode.lo,
+                                    mode.hi, mode.exhaustive, float(S_h[b]))
+            gg = {k: (v if cfg.batch == 1 else v[b]).cpu().numpy()[rows] for k, v in g.items()}
+            assert_same({k: v[None] for k, v in gg.items()}, {k: v[None] for k, v in o.items()},
+                        f"{name} {mode.label} matrix {b}")
+        # flip fraction: the GPU's h against the oracle's h
+        if wm:
+            g2 = nv.scale_search(W, h_oracle_dev.reshape(h_g.shape), S, obj, mode.lo, mode.hi,
+                                 mode.exhaustive, with_stats=False)
+            torch.cuda.synchronize()
+            flips = int((g2["scales"] != g["scales"]).sum())
+            total = g["scales"].numel()
+            print(f"[{name}] {mode.label}: {total} groups, {flips} scale flips with the GPU's h "
+                  f"(fraction {flips / total:.2e}); rows checked bit-exact: "
+                  f"{sum(len(r) for _, r in picks)}", flush=True)
+            assert flips / total < FLIP_MAX
+            moved = float((g["offset"] != 0).float().mean())
+            print(f"[{name}] {mode.label}: {100 * moved:.1f}% of groups leave the max-abs scale",
+                  flush=True)
+        else:
+            print(f"[{name}] {mode.label}: rows checked bit-exact: "
+                  f"{sum(len(r) for _, r in picks)}", flush=True)
+
+
+def test_attn8b(nv):
+    _run_config(nv, "attn8b")
+
+
+def test_down8b(nv):
+    _run_config(nv, "down8b")
+
+
+def test_moe_expert_batch(nv):
+    _run_config(nv, "moe")
+
+
+def test_mlp70b_up(nv):
+    _run_config(nv, "mlp70b_up", sample_rows=24)
+
+
+def test_mlp70b_down(nv):
+    _run_config(nv, "mlp70b_down", sample_rows=12)
