@@ -78,9 +78,8 @@ static nvfp4_status diag_hessian_impl(const void* X, int x_dtype, const int64_t*
     if (seg_offsets == nullptr && segments > 1) return NVFP4_ERR_NULL;
     if ((X && !aligned16(X)) || !aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u)))
         return NVFP4_ERR_ALIGN;
-    const int64_t tiles = nvfp4::hessian_max_tiles(tokens, segments);
-    const int64_t col_tiles = (in + 64 * (16 / esz) - 1) / (64 * (16 / esz));
-    if (tiles * col_tiles >= ((int64_t)1 << 31) || tiles >= ((int64_t)1 << 31))
+    if (nvfp4::hessian_launch_blocks(tokens, in, segments, x_dtype == NVFP4_DTYPE_BF16) >=
+        ((int64_t)1 << 31))
         return NVFP4_ERR_SHAPE;
     const size_t need = nvfp4::hessian_workspace_bytes(tokens, in, segments);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;

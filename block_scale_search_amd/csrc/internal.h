@@ -8,11 +8,9 @@
 
 namespace nvfp4 {
 
-// Diagonal Hessian: rows per partial tile and the tile count bound used for workspace sizing.
-constexpr int kHessRowsPerTile = 512;
-constexpr int kHessWaves = 16;
-int64_t hessian_max_tiles(int64_t tokens, int64_t segments);
+// Diagonal Hessian: workspace bytes and the partial kernel's workgroup count.
 size_t hessian_workspace_bytes(int64_t tokens, int64_t in, int64_t segments);
+int64_t hessian_launch_blocks(int64_t tokens, int64_t in, int64_t segments, bool bf16);
 
 hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t in, int64_t ldx,
                                const int64_t* seg_offsets, int64_t segments, double* h_acc,

@@ -51,12 +51,12 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, float 
     }
 }
 
-// Loss of one code: fixed tree, P_k over elements 4k..4k+3 (first a product, then fmas),
-// L = (P0 + P1) + (P2 + P3).
+// Loss of one code: the weighted squares in element order, L = u0 * d0, then
+// L = fma(u_j, d_j, L) for j = 1..15.
 template <bool WMSE>
 __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)[16], float eff,
                                           float r) {
-    float P[4];
+    float L = 0.0f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         float x[8], q[8];
@@ -69,11 +69,10 @@ __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)
             const float a = fabsf(w[j]);
             const float d = __builtin_fmaf(-q[i], eff, a);
             const float u = WMSE ? h[j] * d : d;
-            if ((j & 3) == 0) P[j >> 2] = u * d;
-            else P[j >> 2] = __builtin_fmaf(u, d, P[j >> 2]);
+            L = (j == 0) ? u * d : __builtin_fmaf(u, d, L);
         }
     }
-    return (P[0] + P[1]) + (P[2] + P[3]);
+    return L;
 }
 
 // Losses of codes c and c + 8 from one multiply per element (valid when both are normal codes
@@ -81,7 +80,7 @@ __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)
 template <bool WMSE>
 __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)[16], float eff,
                                           float r, float eff_hi, float& L_lo, float& L_hi) {
-    float P[4], Q[4];
+    float P = 0.0f, Q = 0.0f;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         float x[8], q[8], s[8];
@@ -97,23 +96,104 @@ __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)
             const float e = __builtin_fmaf(-s[i], eff_hi, a);
             const float u = WMSE ? h[j] * d : d;
             const float v = WMSE ? h[j] * e : e;
-            if ((j & 3) == 0) {
-                P[j >> 2] = u * d;
-                Q[j >> 2] = v * e;
-            } else {
-                P[j >> 2] = __builtin_fmaf(u, d, P[j >> 2]);
-                Q[j >> 2] = __builtin_fmaf(v, e, Q[j >> 2]);
-            }
+            P = (j == 0) ? u * d : __builtin_fmaf(u, d, P);
+            Q = (j == 0) ? v * e : __builtin_fmaf(v, e, Q);
         }
     }
-    L_lo = (P[0] + P[1]) + (P[2] + P[3]);
-    L_hi = (Q[0] + Q[1]) + (Q[2] + Q[3]);
+    L_lo = P;
+    L_hi = Q;
 }
 
-__device__ __forceinline__ void take_min(float L, int c, float& best, int& best_c) {
-    const bool take = (L < best) | ((L == best) & (c < best_c));
+// Running minimum over candidates visited in ascending code order: a strictly smaller loss
+// replaces the best, so the first (lowest) code wins ties.
+__device__ __forceinline__ void keep_min(float L, int c, float& best, int& best_c) {
+    const bool take = L < best;
     best = take ? L : best;
     best_c = take ? c : best_c;
+}
+
+// One block of up to 16 consecutive codes c0 .. c0 + nb - 1 (all normal codes, octave identity
+// holding): codes c0 + p and c0 + p + 8 share one multiply. The low codes (p < 8) and the high
+// codes (p >= 8) are each scanned in ascending order; every high code follows every low code,
+// so the block's first minimum is the low one unless the high one is strictly smaller. The
+// block's result then enters the running minimum the same way. NB > 0 fixes the block length
+// at compile time (full unroll); NB == 0 reads it from nb.
+template <bool WMSE, int NB>
+__device__ __forceinline__ void scan_block(const float (&w)[16], const float (&h)[16],
+                                           const float2* __restrict__ t0, int c0, int nb,
+                                           float& best, int& best_c) {
+    const int n = NB > 0 ? NB : nb;
+    float bl = __builtin_inff(), bh = __builtin_inff();
+    int pl = 0, ph = 8;
+#pragma unroll
+    for (int p = 0; p < (NB > 0 ? (NB < 8 ? NB : 8) : 8); ++p) {
+        if (NB == 0 && p >= n) break;
+        const float2 er = t0[p];
+        if (p + 8 < n) {
+            float L_lo, L_hi;
+            loss_pair<WMSE>(w, h, er.x, er.y, t0[p + 8].x, L_lo, L_hi);
+            if (L_lo < bl) { bl = L_lo; pl = p; }
+            if (L_hi < bh) { bh = L_hi; ph = p + 8; }
+        } else {
+            const float L = loss_one<WMSE>(w, h, er.x, er.y);
+            if (L < bl) { bl = L; pl = p; }
+        }
+    }
+    keep_min(bl, c0 + pl, best, best_c);
+    keep_min(bh, c0 + ph, best, best_c);
+}
+
+// Windowed search of one lane: codes first .. first + n - 1 (the window base + lo .. base + hi).
+// Fast path for the whole wave when every live lane's codes are normal and unclipped.
+template <bool WMSE, int NWIN>
+__device__ __forceinline__ void search_window(const float (&w)[16], const float (&h)[16],
+                                              const float2* __restrict__ tab, bool octave_ok,
+                                              bool live, int first, int n_rt, float& best,
+                                              int& best_c) {
+    const int n = NWIN > 0 ? NWIN : n_rt;
+    // idle lanes score the in-range dummy codes starting at 8
+    const bool lane_fast = live ? (first >= 8 && first + n - 1 <= 126) : (n <= 119);
+    if (octave_ok && __all(lane_fast)) {
+        const int c0 = live ? first : 8;
+        if constexpr (NWIN > 0 && NWIN <= 16) {
+            scan_block<WMSE, NWIN>(w, h, tab + c0, c0, NWIN, best, best_c);
+        } else {
+            for (int blk = 0; blk < n; blk += 16)
+                scan_block<WMSE, 0>(w, h, tab + c0 + blk, c0 + blk, min(16, n - blk), best,
+                                    best_c);
+        }
+        return;
+    }
+    // clipped windows, subnormal codes or a table without the octave identity: every code on
+    // its own, ascending
+    for (int p = 0; p < n; ++p) {
+        const int c = first + p;
+        if (live && c >= 1 && c <= 126) {
+            const float2 er = tab[c];
+            keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+        }
+    }
+}
+
+// Exhaustive search: the subnormal codes 1..7 on their own, then the normal codes 8..126 in
+// blocks of 16 (octave pairs) when the table allows it, all in ascending block order.
+template <bool WMSE>
+__device__ __forceinline__ void search_all(const float (&w)[16], const float (&h)[16],
+                                           const float2* __restrict__ tab, bool octave_ok,
+                                           float& best, int& best_c) {
+    if (!octave_ok) {
+        for (int c = 1; c <= 126; ++c) {
+            const float2 er = tab[c];
+            keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+        }
+        return;
+    }
+    for (int c = 1; c < 8; ++c) {
+        const float2 er = tab[c];
+        keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+    }
+    for (int blk = 8; blk <= 126; blk += 16)
+        scan_block<WMSE, 0>(w, h, tab + blk, blk, min(16, 127 - blk), best, best_c);
 }
 
 // Per-workgroup code table in LDS: tab[c] = (eff[c], r[c]) for c = 1..126, tab[0] = (0, 0).
@@ -141,11 +221,18 @@ __device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
     return *flag == 0;
 }
 
-template <bool BF16, bool WMSE>
+// Row of a flat group index, gi / gpr, as (gi * M) >> (32 + L) with L = ceil(log2 gpr) and
+// M = ceil(2^(32+L) / gpr) < 2^33: the product stays below 2^64 and the error term, below
+// gi / 2^(32+L) < 2^-(L+1) <= 1/(2 gpr), cannot carry the quotient past an integer (gi < 2^31).
+__device__ __forceinline__ uint32_t div_gpr(uint32_t gi, uint64_t magic, uint32_t shift) {
+    return (uint32_t)(((uint64_t)gi * magic) >> shift);
+}
+
+template <bool BF16, bool WMSE, int NWIN>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
-    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, int64_t ldw_bytes,
-    int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h, int lo, int hi,
-    int exhaustive, const float* __restrict__ S_arr, uint8_t* __restrict__ scales,
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
+    uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h,
+    int lo, int hi, int exhaustive, const float* __restrict__ S_arr, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out) {
     __shared__ float2 tab[128];
     __shared__ int flag;
@@ -156,7 +243,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     const uint32_t G = out * gpr;
     const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
     const bool valid = gi < G;
-    const uint32_t row = valid ? gi / gpr : 0u;
+    const uint32_t row = valid ? div_gpr(gi, gpr_magic, gpr_shift) : 0u;
     const uint32_t g = valid ? gi - row * gpr : 0u;
 
     float w[16], h[16];
@@ -193,61 +280,12 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     }
     const bool live = valid && b > 0;
 
-    // Candidate codes: first + p for p = 0..n-1, kept when inside [1, 126].
-    const int n = exhaustive ? 126 : hi - lo + 1;
-    const int first = exhaustive ? 1 : b + lo;
     float best = __builtin_inff();
-    int best_c = 255;
-
-    // Paired window path: every live lane's codes lie in 8..126 (no clipping, no subnormal
-    // codes); idle lanes score the in-range dummy range starting at code 8.
-    const bool lane_fast = live ? (first >= 8 && first + n - 1 <= 126) : (n <= 119);
-    if (!exhaustive && octave_ok && __all(lane_fast)) {
-        const int c0 = live ? first : 8;
-        for (int blk = 0; blk < n; blk += 16) {
-            const int nb = min(16, n - blk);
-            for (int p = 0; p < min(nb, 8); ++p) {
-                const int c = c0 + blk + p;
-                const float2 er = tab[c];
-                if (p + 8 < nb) {
-                    float L_lo, L_hi;
-                    loss_pair<WMSE>(w, h, er.x, er.y, tab[c + 8].x, L_lo, L_hi);
-                    take_min(L_lo, c, best, best_c);
-                    take_min(L_hi, c + 8, best, best_c);
-                } else {
-                    take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
-                }
-            }
-        }
-    } else if (exhaustive && octave_ok) {
-        // Subnormal codes on their own, then the normal codes 8..126 in octave pairs.
-        for (int c = 1; c < 8; ++c) {
-            const float2 er = tab[c];
-            take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
-        }
-        for (int blk = 8; blk <= 126; blk += 16) {
-            const int nb = min(16, 127 - blk);
-            for (int p = 0; p < min(nb, 8); ++p) {
-                const int c = blk + p;
-                const float2 er = tab[c];
-                if (p + 8 < nb) {
-                    float L_lo, L_hi;
-                    loss_pair<WMSE>(w, h, er.x, er.y, tab[c + 8].x, L_lo, L_hi);
-                    take_min(L_lo, c, best, best_c);
-                    take_min(L_hi, c + 8, best, best_c);
-                } else {
-                    take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
-                }
-            }
-        }
+    int best_c = 0;
+    if (exhaustive) {
+        if (__any(live)) search_all<WMSE>(w, h, tab, octave_ok, best, best_c);
     } else {
-        for (int p = 0; p < n; ++p) {
-            const int c = first + p;
-            if (live && c >= 1 && c <= 126) {
-                const float2 er = tab[c];
-                take_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
-            }
-        }
+        search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, b + lo, hi - lo + 1, best, best_c);
     }
     if (!live) {
         best = 0.0f;
@@ -426,21 +464,34 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
                                bool wmse, int lo, int hi, bool exhaustive, const float* S,
                                uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
                                hipStream_t stream) {
-    const int64_t G = out * (in / 16);
+    const int64_t gpr = in / 16;
+    const int64_t G = out * gpr;
+    uint32_t L = 0;
+    while (((int64_t)1 << L) < gpr) ++L;
+    const uint64_t magic = (((uint64_t)1 << (32 + L)) + (uint64_t)gpr - 1) / (uint64_t)gpr;
     const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
     const int esz = bf16 ? 2 : 4;
     const uint8_t* Wb = static_cast<const uint8_t*>(W);
-#define NVFP4_LAUNCH_SEARCH(B, M)                                                                \
-    hipLaunchKernelGGL((k_scale_search<B, M>), grid, dim3(kSearchThreads), 0, stream, Wb,        \
-                       (uint32_t)out, (uint32_t)in, ldw * esz, stride_w * esz, h, stride_h, lo, \
-                       hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset)
+    const int n = hi - lo + 1;
+    const int nwin = exhaustive ? 0 : (n == 16 ? 16 : (n == 11 ? 11 : 0));
+#define NVFP4_LAUNCH_SEARCH(B, M, N)                                                              \
+    hipLaunchKernelGGL((k_scale_search<B, M, N>), grid, dim3(kSearchThreads), 0, stream, Wb,      \
+                       (uint32_t)out, (uint32_t)in, magic, 32 + L, ldw * esz, stride_w * esz, h,  \
+                       stride_h, lo, hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset)
+#define NVFP4_LAUNCH_SEARCH_N(B, M)                                                               \
+    do {                                                                                          \
+        if (nwin == 16) NVFP4_LAUNCH_SEARCH(B, M, 16);                                            \
+        else if (nwin == 11) NVFP4_LAUNCH_SEARCH(B, M, 11);                                       \
+        else NVFP4_LAUNCH_SEARCH(B, M, 0);                                                        \
+    } while (0)
     if (bf16) {
-        if (wmse) NVFP4_LAUNCH_SEARCH(true, true);
-        else NVFP4_LAUNCH_SEARCH(true, false);
+        if (wmse) NVFP4_LAUNCH_SEARCH_N(true, true);
+        else NVFP4_LAUNCH_SEARCH_N(true, false);
     } else {
-        if (wmse) NVFP4_LAUNCH_SEARCH(false, true);
-        else NVFP4_LAUNCH_SEARCH(false, false);
+        if (wmse) NVFP4_LAUNCH_SEARCH_N(false, true);
+        else NVFP4_LAUNCH_SEARCH_N(false, false);
     }
+#undef NVFP4_LAUNCH_SEARCH_N
 #undef NVFP4_LAUNCH_SEARCH
     return hipGetLastError();
 }

@@ -129,8 +129,8 @@ nvfp4_status nvfp4_global_scale(const void* W, int w_dtype, int64_t batch, int64
  *            WMSE in FP8 bit-pattern space), or all codes 1..126 if exhaustive ([SS] §2)
  *   loss(c) = sum_j u_j * d_j, x_j = fl(|w_j| * r[c]), q_j = E2M1_RNE(x_j) (ties to the even
  *            code, saturating at 6), d_j = fma(-q_j, eff[c], |w_j|), u_j = fl(h_j * d_j) for
- *            WMSE or d_j for MSE, summed as four fma chains over j = 4k..4k+3 then
- *            (P0 + P1) + (P2 + P3) in binary32
+ *            WMSE or d_j for MSE, summed in element order in binary32: L = u_0 d_0, then
+ *            L = fma(u_j, d_j, L) for j = 1..15
  *   choice = the code of smallest loss, the lowest code among equal losses ([SR] App. D.2:
  *            ties are deterministic)
  *   output ([HS] App. B: quantize once with the chosen scale, native NVFP4):

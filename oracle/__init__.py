@@ -13,7 +13,7 @@ source. Parity status of each part:
 * E2M1 rounding, E4M3 encode/decode, h, global scale, base code, candidate loss and argmin:
   pinned by the checks in ``tests/test_oracle_*.py`` (closed forms, a library routine,
   exact-rational recomputation, brute force, and the bounds the ScaleSweep page states).
-* Nibble order inside a byte (low nibble = even element) and the fixed fp32 summation tree:
+* Nibble order inside a byte (low nibble = even element) and the binary32 operation order:
   conventions the pages do not fix. The nibble contents are pinned by a dequantisation round
   trip; the byte order itself is "parity unpinned".
 """

@@ -29,8 +29,8 @@
  *     or a caller-given S. S = 1 for an all-zero tensor.
  *   - Effective scale eff[c] = fl(S * dec(c)); its reciprocal r[c] = fl(1 / eff[c]); a weight is
  *     normalised as fl(|w| * r[c]).
- *   - Residual d = fma(-q, eff, |w|); loss in a fixed 4x4 tree (below); the first strictly
- *     smaller loss wins, so ties go to the lowest offset.
+ *   - Residual d = fma(-q, eff, |w|); the weighted squares are summed with fmas in element
+ *     order; the first strictly smaller loss wins, so ties go to the lowest offset.
  *   - Nibble = sign(w) << 3 | E2M1 index; two nibbles per byte, low nibble first.
  */
 #include <math.h>
@@ -182,22 +182,19 @@ int ref_scale_tables(float S, float* eff, float* rcp)
  * reconstruction objective; [SS] §1: MSE and WMSE). For element j:
  *   x_j = fl(|w_j| * r),  q_j = E2M1(x_j),  d_j = fma(-q_j, eff, |w_j|),
  *   u_j = fl(h_j * d_j) (WMSE) or d_j (MSE).
- * The 16 products u_j * d_j are summed as four chains of four (P_k over j = 4k..4k+3, the first
- * a plain product, the rest fused multiply-adds), then (P0 + P1) + (P2 + P3). */
+ * The 16 products u_j * d_j are summed in element order: L = fl(u_0 * d_0), then
+ * L = fma(u_j, d_j, L) for j = 1..15. */
 static float group_loss(const float a[16], const float* h, float eff, float r)
 {
-    float P[4];
-    for (int k = 0; k < 4; ++k) {
-        for (int i = 0; i < 4; ++i) {
-            int j = 4 * k + i;
-            float x = a[j] * r;
-            float q = E2M1_LEVEL[ref_e2m1_index(x)];
-            float d = fmaf(-q, eff, a[j]);
-            float u = h ? h[j] * d : d;
-            P[k] = (i == 0) ? u * d : fmaf(u, d, P[k]);
-        }
+    float L = 0.0f;
+    for (int j = 0; j < 16; ++j) {
+        float x = a[j] * r;
+        float q = E2M1_LEVEL[ref_e2m1_index(x)];
+        float d = fmaf(-q, eff, a[j]);
+        float u = h ? h[j] * d : d;
+        L = (j == 0) ? u * d : fmaf(u, d, L);
     }
-    return (P[0] + P[1]) + (P[2] + P[3]);
+    return L;
 }
 
 /* Base code of a group: the E4M3-rounded absmax/6 in units of S ([SS] Problem Statement and §2:

@@ -249,13 +249,35 @@ def test_workspace_reuse(nv):
             o0, o1 = int(offs[e]), int(offs[e + 1])
             want = oracle.diag_hessian(Xn[o0:o1])[0] if o1 > o0 else np.zeros(n)
             np.testing.assert_allclose(acc[e * n:(e + 1) * n].cpu().numpy(), want, rtol=1e-12)
-    wss = torch.full((nv.nvfp4_global_scale_workspace_size(1, 4096, 4096),), 0xA5, dtype=torch.uint8,
+    wss = torch.zeros((nv.nvfp4_global_scale_workspace_size(1, 4096, 4096),), dtype=torch.uint8,
                       device=DEV)
     for out, inp, dt in ((512, 4096, torch.bfloat16), (64, 512, torch.float32), (4096, 4096, torch.bfloat16)):
         W = _mat(out, inp, dt, seed=out + inp)
         S = torch.empty(1, dtype=torch.float32, device=DEV)
         nv.nvfp4_global_scale(W, 1, out, inp, inp, out * inp, nv.GS_AMAX_448, S, wss)
         assert S.item() == np.float32(oracle.global_scale(host_w(W), oracle.GS_AMAX_448))
+
+
+def test_global_scale_many_calls(nv):
+    """Many back-to-back global-scale calls (1-4 matrices, both element types) on one reused
+    workspace, against the oracle each time."""
+    ws = torch.zeros(nv.nvfp4_global_scale_workspace_size(4, 64 + 17 * 60, 512), dtype=torch.uint8,
+                     device=DEV)
+    mats, outs = [], []
+    for i in range(60):
+        b = 1 + i % 4
+        W = _mat(64 + 17 * i, 512, torch.bfloat16 if i % 2 else torch.float32, seed=900 + i,
+                 batch=None if b == 1 else b)
+        bb, o, n = (1,) + tuple(W.shape) if W.dim() == 2 else tuple(W.shape)
+        S = torch.empty(bb, dtype=torch.float32, device=DEV)
+        nv.nvfp4_global_scale(W, bb, o, n, n, o * n, nv.GS_AMAX_256, S, ws)
+        mats.append(W)
+        outs.append(S)
+    torch.cuda.synchronize()
+    for W, S in zip(mats, outs):
+        Wb = W if W.dim() == 3 else W[None]
+        for b in range(Wb.shape[0]):
+            assert S[b].item() == np.float32(oracle.global_scale(host_w(Wb[b]), oracle.GS_AMAX_256))
 
 
 def test_global_scale_rules_and_batch(nv):
