@@ -3,6 +3,11 @@
 One step = the whole path over one synthetic layer held in HBM:
   diagonal Hessian over X -> global scale of W -> scale search + pack for every mode the
   workload names (attn8b: MSE [-3,7] and WMSE [-8,7]).
+With --streams 2 the h-reduce runs on a second stream (same default priority), overlapping the
+global scale and the searches that do not read h; the searches that read h wait for it. The
+default is one stream, so that every kernel's time is its own.
+After the timed steps, the pack-at-given-scales entry point (not part of a step) is timed on
+its own over the same layers, with the scale bytes the last search wrote.
 Prints one JSON line. `value` is weight-searches per second: every mode run searches each of the
 layer's weights once, so a step counts n_weights * n_modes. Several input sets are rotated
 (more bytes than the 256 MB MALL) so that every step reads its inputs from HBM.
@@ -96,30 +101,38 @@ class Runner:
                                 dtype=torch.uint8, device=dev)
         self.rule = nvfp4.GS_AMAX_256 if cfg.gs_rule == "amax256" else nvfp4.GS_AMAX_448
 
-    def calls(self, s: Layer):
-        """The step as a list of (label, call) pairs in stream order; each call is a prepared
-        C-ABI invocation (arguments marshalled once) on the current stream."""
+    def calls(self, s: Layer, aux=None):
+        """The step as (label, call, stream_role) triples in issue order; each call is a prepared
+        C-ABI invocation (arguments marshalled once). With an auxiliary stream, the h-reduce
+        runs there ("aux") while the main stream computes the global scale and the searches
+        that do not read h; the searches that read h wait for it ("main_after_h")."""
         nv, cfg = self.nv, self.cfg
         b, o, n = cfg.batch, cfg.out, cfg.inp
         ldw, sw = n, o * n
         out = []
+        import torch
+        hs = aux if aux is not None else torch.cuda.current_stream()
         for ci, X in enumerate(s.chunks):
             T = X.shape[0]
             if s.seg is not None:
                 out.append(("h_reduce", nv.nvfp4_diag_hessian_batched(
-                    X, s.seg, b, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, prepare=True)))
+                    X, s.seg, b, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, stream=hs,
+                    prepare=True), "aux"))
             else:
                 out.append(("h_reduce", nv.nvfp4_diag_hessian(
-                    X, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, prepare=True)))
+                    X, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, stream=hs, prepare=True),
+                    "aux"))
         out.append(("global_scale", nv.nvfp4_global_scale(
-            s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True)))
+            s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
         for mi, m in enumerate(cfg.modes):
             wm = m.objective == "wmse"
             out.append((f"search:{m.label}", nv.nvfp4_scale_search(
                 s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
                 nv.WMSE if wm else nv.MSE, m.lo, m.hi, m.exhaustive, s.S, s.scales[mi],
-                s.packed[mi], prepare=True)))
-        return out
+                s.packed[mi], prepare=True), "main_after_h" if wm else "main"))
+        # issue order: aux work first, then main work that does not need h, then the rest
+        rank = {"aux": 0, "main": 1, "main_after_h": 2}
+        return sorted(out, key=lambda t: rank[t[2]])
 
 
 def algorithmic(cfg, label: str):
@@ -193,6 +206,9 @@ def main():
     ap.add_argument("--workload", default="attn8b")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = enough for >1 GB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
+                    help="2: h-reduce on a second stream, overlapping the global scale and the "
+                         "searches that do not read h")
     ap.add_argument("--events-every", type=int, default=8,
                     help="record per-call HIP events on every Nth timed step (1 = all)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -223,36 +239,74 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
-    steps = [runner.calls(s) for s in runner.sets]
-    for i in range(args.warmup):
-        for _, f in steps[i % n_sets]:
+    main = torch.cuda.current_stream()
+    aux = torch.cuda.Stream() if args.streams == 2 else None
+    steps = [runner.calls(s, aux) for s in runner.sets]
+
+    def run_step(calls, timed_row=None):
+        """One step. Two streams: the aux stream starts when the step starts (event), the
+        main stream waits for the aux work before the searches that read h."""
+        if aux is not None:
+            aux.wait_stream(main)
+        waited = False
+        for lab, f, role in calls:
+            st = aux if (aux is not None and role == "aux") else main
+            if aux is not None and role == "main_after_h" and not waited:
+                main.wait_stream(aux)
+                waited = True
+            if timed_row is None:
+                f()
+                continue
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(st)
             f()
+            e1.record(st)
+            timed_row.append((e0, e1))
+        if aux is not None and not waited:
+            main.wait_stream(aux)
+
+    for i in range(args.warmup):
+        run_step(steps[i % n_sets])
     torch.cuda.synchronize()
 
-    labels = [lab for lab, _ in steps[0]]
+    labels = [lab for lab, _, _ in steps[0]]
     ev = []
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record()
+    t_start.record(main)
     for i in range(args.steps):
         if i % args.events_every:
-            for _, f in steps[i % n_sets]:
-                f()
+            run_step(steps[i % n_sets])
             continue
         row = []
-        for _, f in steps[i % n_sets]:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            f()
-            e1.record()
-            row.append((e0, e1))
+        run_step(steps[i % n_sets], row)
         ev.append(row)
-    t_end.record()
+    t_end.record(main)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    # pack at given scales: outside the step, timed on its own (events on the main stream)
+    nv = runner.nv
+    packs = []
+    for s_ in runner.sets:
+        o_, n_ = cfg.out, cfg.inp
+        packs.append(nv.nvfp4_pack(s_.W, cfg.batch, o_, n_, n_, o_ * n_, s_.scales[-1], s_.S,
+                                   s_.packed[-1], prepare=True))
+    for f in packs:
+        f()
+    torch.cuda.synchronize()
+    p0 = torch.cuda.Event(enable_timing=True)
+    p1 = torch.cuda.Event(enable_timing=True)
+    reps = 50 * n_sets
+    p0.record(main)
+    for i in range(reps):
+        packs[i % n_sets]()
+    p1.record(main)
+    torch.cuda.synchronize()
+    pack_us = p0.elapsed_time(p1) * 1e3 / reps
 
     per_label = {}
     for row in ev:
@@ -270,6 +324,12 @@ def main():
             k["TFLOP/s"] = round(nf / us_avg / 1e6, 2)
             k["frac_valu_78.6"] = round(nf / us_avg / 1e6 / VALU_PEAK_TFLOPS, 4)
         kernels[lab] = k
+    wb = 2 if str(cfg.w_dtype).endswith("bfloat16") else 4
+    pack_bytes = cfg.n_weights * wb + cfg.n_weights // 2 + cfg.n_weights // 16
+    kernels["pack (outside the step)"] = {
+        "avg_us": round(pack_us, 3), "calls_per_step": 0, "alg_bytes": pack_bytes,
+        "GB/s": round(pack_bytes / pack_us / 1e3, 1),
+        "frac_hbm": round(pack_bytes / pack_us / 1e3 / HBM_PEAK_GBS, 4)}
     dom = max((l for l in kernels if l.startswith("search")),
               key=lambda l: kernels[l]["avg_us"] * kernels[l]["calls_per_step"])
     nb, nf = algorithmic(cfg, dom)
@@ -309,7 +369,8 @@ def main():
         "data": "synthetic (seeded; stands in for the pages' calibration sets and checkpoints)",
         "config": {"workload": cfg.description, "name": cfg.name,
                    "modes": [m.label for m in cfg.modes], "global_scale": cfg.gs_rule,
-                   "weights_per_step": searched, "input_sets_rotated": n_sets},
+                   "weights_per_step": searched, "input_sets_rotated": n_sets,
+                   "streams": args.streams},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
