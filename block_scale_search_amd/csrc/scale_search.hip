@@ -175,25 +175,128 @@ __device__ __forceinline__ void search_window(const float (&w)[16], const float 
     }
 }
 
-// Exhaustive search: the subnormal codes 1..7 on their own, then the normal codes 8..126 in
-// blocks of 16 (octave pairs) when the table allows it, all in ascending block order.
+// Lexicographic running minimum on (loss, code): the result of a scan that visits codes in any
+// order equals the ascending scan's first minimum.
+__device__ __forceinline__ void keep_min_lex(float L, int c, float& best, int& best_c) {
+    const bool take = L < best || (L == best && c < best_c);
+    best = take ? L : best;
+    best_c = take ? c : best_c;
+}
+
+// Lower bounds of the loss over a whole range of codes, from one code's effective scale eff.
+//  - Codes at or below the code of eff (eff' <= eff): an element with a > 6 eff saturates at
+//    every such code, so its residual is at least a - 6 eff.
+//  - Codes at or above it (eff' >= eff): an element with a < eff / 2 rounds either to 0 (residual
+//    a) or to a level of at least eff' / 2 (residual at least eff / 2 - a).
+// Both bound sums grow monotonically away from eff, so one test prunes every code beyond.
+template <bool WMSE>
+__device__ __forceinline__ float bound_below(const float (&w)[16], const float (&h)[16],
+                                             float eff) {
+    float B = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float t = fmaxf(__builtin_fmaf(-6.0f, eff, fabsf(w[j])), 0.0f);
+        B = WMSE ? __builtin_fmaf(h[j] * t, t, B) : __builtin_fmaf(t, t, B);
+    }
+    return B;
+}
+
+template <bool WMSE>
+__device__ __forceinline__ float bound_above(const float (&w)[16], const float (&h)[16],
+                                             float eff) {
+    const float half = 0.5f * eff;
+    float B = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const float a = fabsf(w[j]);
+        const float t = a < half ? fminf(a, half - a) : 0.0f;
+        B = WMSE ? __builtin_fmaf(h[j] * t, t, B) : __builtin_fmaf(t, t, B);
+    }
+    return B;
+}
+
+// Eight codes c0 .. c0 + 7 of one lane, each on its own; codes outside 1..126 are skipped.
+template <bool WMSE>
+__device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16],
+                                      const float2* __restrict__ tab, int c0, float& best,
+                                      int& best_c) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const int c = c0 + p;
+        const bool in = c >= 1 && c <= 126;
+        const float2 er = tab[in ? c : 1];
+        const float L = loss_one<WMSE>(w, h, er.x, er.y);
+        if (in) keep_min_lex(L, c, best, best_c);
+    }
+}
+
+// Exhaustive search over all 126 codes, with pruning that provably skips only losers.
+// Each lane first scores the 16 codes around its own base code (octave pairs when the table
+// allows), then extends upward and downward in blocks of 8 codes while the loss bounds above
+// cannot exclude the next code. A bound prunes a direction when it exceeds the best loss by a
+// relative margin of 2^-14, which covers the rounding of the binary32 loss chain and of the
+// bound itself (each at most about 20 roundings of 2^-24 on sums of non-negative terms). The
+// test is used only where that error analysis holds: non-negative finite h, a best loss of at
+// least 2^-100 and amax (1 + max h) <= 2^100 best, so that underflowing products (absolute
+// error 2^-150 each) stay far below the margin; elsewhere the lane scans every code. The result
+// equals the ascending scan of all 126 codes with the first minimum kept.
 template <bool WMSE>
 __device__ __forceinline__ void search_all(const float (&w)[16], const float (&h)[16],
                                            const float2* __restrict__ tab, bool octave_ok,
-                                           float& best, int& best_c) {
-    if (!octave_ok) {
-        for (int c = 1; c <= 126; ++c) {
-            const float2 er = tab[c];
-            keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+                                           bool live, int b, float& best, int& best_c) {
+    float amax = 0.0f, hmax = 1.0f;
+    bool h_ok = true;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        amax = fmaxf(amax, fabsf(w[j]));
+        if (WMSE) {
+            hmax = fmaxf(hmax, h[j]);
+            h_ok = h_ok && h[j] >= 0.0f && h[j] <= 0x1p100f;
         }
-        return;
     }
-    for (int c = 1; c < 8; ++c) {
-        const float2 er = tab[c];
-        keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+    const float scale_ref = amax * (1.0f + hmax);
+
+    // centre block: 16 codes from c0 (at least 8 and at most 111 so that pairs stay normal)
+    const int c0 = live ? min(max(b - 8, 8), 111) : 8;
+    if (octave_ok) {
+        scan_block<WMSE, 16>(w, h, tab + c0, c0, 16, best, best_c);
+    } else {
+        scan8<WMSE>(w, h, tab, c0, best, best_c);
+        scan8<WMSE>(w, h, tab, c0 + 8, best, best_c);
     }
-    for (int blk = 8; blk <= 126; blk += 16)
-        scan_block<WMSE, 0>(w, h, tab + blk, blk, min(16, 127 - blk), best, best_c);
+    int up = c0 + 16, dn = c0 - 1;  // next unscored code in each direction
+    bool up_done = !live || up > 126;
+    bool dn_done = !live || dn < 1;
+    while (true) {
+        const bool can_prune = h_ok && best >= 0x1p-100f && scale_ref <= best * 0x1p100f;
+        const float thr = __builtin_fmaf(best, 0x1p-14f, best);
+        if (!up_done && can_prune) {
+            const float B = bound_above<WMSE>(w, h, tab[up].x);
+            up_done = B > thr && B <= 0x1.fffffep127f;
+        }
+        if (up_done && !dn_done && can_prune) {
+            const float B = bound_below<WMSE>(w, h, tab[dn].x);
+            dn_done = B > thr && B <= 0x1.fffffep127f;
+        }
+        const bool go_up = !up_done;
+        const bool go_dn = up_done && !dn_done;
+        if (!__any(go_up || go_dn)) break;
+        const int first = go_up ? up : (go_dn ? dn - 7 : 8);
+        float bl = best;
+        int cl = best_c;
+        scan8<WMSE>(w, h, tab, first, bl, cl);
+        if (go_up || go_dn) {
+            best = bl;
+            best_c = cl;
+        }
+        if (go_up) {
+            up += 8;
+            up_done = up > 126;
+        } else if (go_dn) {
+            dn -= 8;
+            dn_done = dn < 1;
+        }
+    }
 }
 
 // Per-workgroup code table in LDS: tab[c] = (eff[c], r[c]) for c = 1..126, tab[0] = (0, 0).
@@ -280,10 +383,12 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     }
     const bool live = valid && b > 0;
 
+    // The running best starts at +inf with the first candidate's code, so a group whose every
+    // loss overflows keeps its first candidate, as the ascending scan does.
     float best = __builtin_inff();
-    int best_c = 0;
+    int best_c = exhaustive ? 1 : min(max(b + lo, 1), 126);
     if (exhaustive) {
-        if (__any(live)) search_all<WMSE>(w, h, tab, octave_ok, best, best_c);
+        if (__any(live)) search_all<WMSE>(w, h, tab, octave_ok, live, b, best, best_c);
     } else {
         search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, b + lo, hi - lo + 1, best, best_c);
     }

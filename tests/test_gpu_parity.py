@@ -132,6 +132,25 @@ def test_edge_groups(nv):
     assert base[4, 1] == 126 and base[6].max() == 1
 
 
+def test_overflowing_losses_and_negative_h(nv):
+    """Groups whose every candidate loss overflows to +inf keep their first candidate (the
+    ascending scan never finds a strictly smaller loss), and a caller's h with negative entries
+    (losses no longer sums of non-negative terms) still matches the oracle in every mode."""
+    out, inp = 48, 256
+    W = _mat(out, inp, torch.float32, seed=71)
+    h = _h(inp, seed=72, spread=2.0)
+    W[:16] *= 1e4
+    hh = h.clone()
+    hh[:64] = 3e38                                             # first 4 groups of rows 0..15 overflow
+    hh[100:140] *= -1.0                                        # negative weights in other groups
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    for lo, hi, exh in ((-9, 6, False), (-8, 7, False), (0, 0, True), (-2, 1, False)):
+        g = gpu_search(nv, W, hh, S, "wmse", lo, hi, exh)
+        o = oracle_search(W, hh.cpu().numpy(), S.item(), "wmse", lo, hi, exh)
+        assert_same(g, o, f"overflow/negative h [{lo},{hi}] exh={exh}")
+    assert np.isinf(g["loss"][0, :16, :4]).all()
+
+
 def test_tiny_global_scale_subnormal_codes(nv):
     """A global scale so small that the lowest codes' effective scales are subnormal binary32
     values (their reciprocals still finite), with h large enough that losses do not flush."""
@@ -145,6 +164,31 @@ def test_tiny_global_scale_subnormal_codes(nv):
         o = oracle_search(W, h.cpu().numpy() if obj == "wmse" else None, S.item(), obj, lo, hi,
                           exh)
         assert_same(g, o, f"tiny S {obj} exh={exh}")
+
+
+@pytest.mark.parametrize("s_scale", [1.0, 1e-3, 30.0])
+def test_exhaustive_pruning_boundaries(nv, s_scale):
+    """Exhaustive mode against the oracle where its exact prunings bite differently per lane:
+    groups whose largest weight has h = 0 (no lower bound, deep contractions can win), huge h at
+    the largest weight (early stop), all-small groups (constant top region reached early),
+    and global scales that move the top region towards either end of the code range."""
+    out, inp = 96, 256
+    W = _mat(out, inp, torch.float32, seed=61)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(62)
+    h = torch.exp(torch.randn(inp, generator=g, device=DEV) * 3.0)
+    Wg = W.view(out, inp // 16, 16)
+    imax = Wg.abs().argmax(-1)                               # column of each group's max
+    cols = (torch.arange(inp // 16, device=DEV) * 16)[None, :] + imax
+    hz = h.clone()
+    hz[cols[::3].reshape(-1)] = 0.0                          # every third row: h = 0 at the max
+    hz[cols[1::3].reshape(-1)] *= 1e6                        # next: h huge at the max
+    W[2::3] *= 1e-3                                          # last: tiny groups
+    S = nv.global_scale(W, nv.GS_AMAX_448) * s_scale
+    for obj, hh in (("wmse", hz), ("mse", None)):
+        gg = gpu_search(nv, W, hh, S, obj, 0, 0, True)
+        o = oracle_search(W, None if hh is None else hh.cpu().numpy(), S.item(), obj, 0, 0, True)
+        assert_same(gg, o, f"exhaustive {obj} S x{s_scale}")
 
 
 def test_pack_parity_and_window_zero(nv):
