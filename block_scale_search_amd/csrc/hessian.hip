@@ -2,14 +2,15 @@
 // ([HS] §3 / App. B: h = diag(X^T X); [SR] §3).
 //
 // Two kernels, no atomics, fixed combination order:
-//   partial:  a 256-thread workgroup owns one (column strip, row group). A lane reads 16 B of a
-//             row (8 bf16 or 4 f32 columns), so a wave reads one contiguous 1 KB row segment
-//             and the 4 waves read 4 consecutive rows. The row groups of a segment take its
-//             4-row blocks round-robin (group g: blocks g, g + RG, g + 2 RG, ...), so at any
-//             time the whole grid streams one band of full rows; each lane keeps 4 loads in
-//             flight. Squares are exact in binary64 and summed in binary64; the 4 waves are
-//             combined in wave order through LDS into one binary64 partial per column and
-//             row group. About 512 workgroups are launched in all (2 per CU).
+//   partial:  a workgroup of V waves (V = 8 for X below 256 MiB, else 4) owns one (column
+//             strip, row group). A lane reads 16 B of a row (8 bf16 or 4 f32 columns), so a
+//             wave reads one contiguous 1 KB row segment and the V waves read V consecutive
+//             rows. The row groups of a segment take its V-row blocks round-robin (group g:
+//             blocks g, g + RG, g + 2 RG, ...), so at any time the whole grid streams one band
+//             of full rows; each lane keeps 4 non-temporal loads in flight (X is read once).
+//             Squares are exact in binary64 and summed in binary64; the waves are combined in
+//             wave order through LDS into one binary64 partial per column and row group. About
+//             512 workgroups are launched in all (2 per CU).
 //   finalize: eight threads per (segment, column) add interleaved row-group partials with 8
 //             loads in flight each, combine in a fixed order, add the running sum h_acc and
 //             round once to binary32.
@@ -23,10 +24,17 @@
 namespace nvfp4 {
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;  // 256
 constexpr int kLoads = 4;              // loads in flight per lane
 constexpr int kTargetGroups = 512;     // workgroups per launch (all strips)
+constexpr int64_t kWideBytes = (int64_t)256 << 20;  // X from this size up: 4-wave workgroups
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte load marked non-temporal (streamed once, not kept in the caches).
+__device__ __forceinline__ uint4 load_stream(const uint8_t* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
 
 template <bool BF16>
 struct XCols {
@@ -106,14 +114,14 @@ __global__ __launch_bounds__(256) void k_hess_group_prefix(const int64_t* __rest
     }
 }
 
-template <bool BF16>
-__global__ __launch_bounds__(kThreads) void k_hess_partial(const uint8_t* __restrict__ X,
-                                                           int64_t in, int64_t ldx_bytes,
-                                                           GroupMap map, int64_t n_strips,
-                                                           double* __restrict__ partial) {
+template <bool BF16, int V>
+__global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restrict__ X,
+                                                         int64_t in, int64_t ldx_bytes,
+                                                         GroupMap map, int64_t n_strips,
+                                                         double* __restrict__ partial) {
     constexpr int C = XCols<BF16>::kCols;
     constexpr int SW = XCols<BF16>::kStrip;
-    __shared__ double red[kWaves][SW];
+    __shared__ double red[V][SW];
 
     const int64_t strip = blockIdx.x % n_strips;
     const int64_t grp = blockIdx.x / n_strips;
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_hess_partial(const uint8_t* __rest
     const int64_t col = strip * SW + (int64_t)lane * C;
     const bool active = col < in;
     const uint8_t* base = X + col * (BF16 ? 2 : 4);
-    const int64_t blocks = (row1 - row0 + kWaves - 1) / kWaves;  // 4-row blocks
+    const int64_t blocks = (row1 - row0 + V - 1) / V;  // V-row blocks
 
     double acc[C];
 #pragma unroll
@@ -134,9 +142,9 @@ __global__ __launch_bounds__(kThreads) void k_hess_partial(const uint8_t* __rest
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
             const int64_t j = j0 + (int64_t)k * count;
-            const int64_t r = row0 + j * kWaves + wave;
+            const int64_t r = row0 + j * V + wave;
             if (active && j < blocks && r < row1)
-                v[k] = *reinterpret_cast<const uint4*>(base + r * ldx_bytes);
+                v[k] = load_stream(base + r * ldx_bytes);
             else
                 v[k] = make_uint4(0u, 0u, 0u, 0u);
         }
@@ -162,9 +170,11 @@ __global__ __launch_bounds__(kThreads) void k_hess_partial(const uint8_t* __rest
 #pragma unroll
     for (int i = 0; i < C; ++i) red[wave][lane * C + i] = acc[i];
     __syncthreads();
-    for (int t = threadIdx.x; t < SW; t += kThreads) {
+    for (int t = threadIdx.x; t < SW; t += 64 * V) {
         const int64_t c = strip * SW + t;
-        const double s = ((red[0][t] + red[1][t]) + red[2][t]) + red[3][t];
+        double s = red[0][t];
+#pragma unroll
+        for (int q = 1; q < V; ++q) s += red[q][t];
         if (c < in) partial[grp * in + c] = s;
     }
 }
@@ -229,7 +239,7 @@ int64_t strips_for(int64_t in, bool bf16) {
 int64_t rows_per_group(int64_t tokens, int64_t in, bool bf16) {
     const int64_t want = (tokens * strips_for(in, bf16) + kTargetGroups - 1) / kTargetGroups;
     const int64_t r = want < 16 ? 16 : want;
-    return (r + kWaves - 1) / kWaves * kWaves;
+    return (r + 7) / 8 * 8;
 }
 
 size_t prefix_bytes(int64_t segments) {
@@ -274,13 +284,22 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
     const int64_t blocks = n_strips * max_groups(tokens, in, E, bf16);
     const int64_t ldx_bytes = ldx * (bf16 ? 2 : 4);
     const uint8_t* Xb = static_cast<const uint8_t*>(X);
+    // measured on MI355X: 8-wave workgroups stream small X faster, 4-wave ones large X
+    const bool wide = tokens * in * (bf16 ? 2 : 4) >= kWideBytes;
     if (blocks > 0) {
-        if (bf16)
-            hipLaunchKernelGGL(k_hess_partial<true>, dim3((uint32_t)blocks), dim3(kThreads), 0,
-                               stream, Xb, in, ldx_bytes, map, n_strips, partial);
+        const dim3 grid((uint32_t)blocks);
+        if (bf16 && wide)
+            hipLaunchKernelGGL((k_hess_partial<true, 4>), grid, dim3(256), 0, stream, Xb, in,
+                               ldx_bytes, map, n_strips, partial);
+        else if (bf16)
+            hipLaunchKernelGGL((k_hess_partial<true, 8>), grid, dim3(512), 0, stream, Xb, in,
+                               ldx_bytes, map, n_strips, partial);
+        else if (wide)
+            hipLaunchKernelGGL((k_hess_partial<false, 4>), grid, dim3(256), 0, stream, Xb, in,
+                               ldx_bytes, map, n_strips, partial);
         else
-            hipLaunchKernelGGL(k_hess_partial<false>, dim3((uint32_t)blocks), dim3(kThreads), 0,
-                               stream, Xb, in, ldx_bytes, map, n_strips, partial);
+            hipLaunchKernelGGL((k_hess_partial<false, 8>), grid, dim3(512), 0, stream, Xb, in,
+                               ldx_bytes, map, n_strips, partial);
     }
     const dim3 fgrid((uint32_t)((in + kFinCols - 1) / kFinCols), (uint32_t)E);
     hipLaunchKernelGGL(k_hess_finalize, fgrid, dim3(kFinThreads), 0, stream, partial, in, map,

@@ -451,10 +451,11 @@ __global__ __launch_bounds__(kSearchThreads) void k_pack(
 
 // Global scale: S = amax / 2688 (448 * 6) or amax / 1536 (256 * 6), S = 1 if amax = 0.
 // max |w| is taken on binary32 bit patterns of non-negative values (ordered like unsigned
-// integers): exact and independent of order. Pass 1: each workgroup reduces its share (8 loads
-// of 16 B in flight per lane) to one partial. Pass 2: one workgroup per matrix reduces the
-// partials and writes S.
+// integers): exact and independent of order. Pass 1: each workgroup reduces its share (8
+// non-temporal loads of 16 B in flight per lane) to one partial. Pass 2: one workgroup per
+// matrix reduces the partials and writes S.
 constexpr int kAmaxThreads = 256;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kAmaxLoads = 8;
 constexpr int kAmaxMaxBlocks = 1024;
 
@@ -508,7 +509,8 @@ __global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const uint8_t* __
             d[k] = make_uint4(0u, 0u, 0u, 0u);
             if (v < nvec) {
                 const int64_t off = dense ? v * 16 : (v / vpr) * ldw_bytes + (v % vpr) * 16;
-                d[k] = *reinterpret_cast<const uint4*>(base + off);
+                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
+                d[k] = make_uint4(t.x, t.y, t.z, t.w);
             }
         }
 #pragma unroll
