@@ -61,4 +61,11 @@ __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t word, float x0, float x1
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(word, x0, x1, 1.0f, SEL);
 }
 
+// Row of a flat group index, gi / gpr, as (gi * M) >> (32 + L) with L = ceil(log2 gpr) and
+// M = ceil(2^(32+L) / gpr) < 2^33: the product stays below 2^64 and the error term, below
+// gi / 2^(32+L) < 2^-(L+1) <= 1/(2 gpr), cannot carry the quotient past an integer (gi < 2^31).
+__device__ __forceinline__ uint32_t div_gpr(uint32_t gi, uint64_t magic, uint32_t shift) {
+    return (uint32_t)(((uint64_t)gi * magic) >> shift);
+}
+
 }  // namespace nvfp4

@@ -8,6 +8,14 @@
 
 namespace nvfp4 {
 
+// Magic multiplier and shift for div_gpr (device_formats.h): gi / gpr for 0 <= gi < 2^31.
+inline void gpr_divisor(int64_t gpr, uint64_t& magic, uint32_t& shift) {
+    uint32_t L = 0;
+    while (((int64_t)1 << L) < gpr) ++L;
+    magic = (((uint64_t)1 << (32 + L)) + (uint64_t)gpr - 1) / (uint64_t)gpr;
+    shift = 32 + L;
+}
+
 // Diagonal Hessian: workspace bytes and the partial kernel's workgroup count.
 size_t hessian_workspace_bytes(int64_t tokens, int64_t in, int64_t segments);
 int64_t hessian_launch_blocks(int64_t tokens, int64_t in, int64_t segments, bool bf16);

@@ -1,5 +1,4 @@
-// Global scale, fused per-group E4M3 scale search + E2M1 quantize + pack, and pack at given
-// scales, for gfx950.
+// Fused per-group E4M3 scale search + E2M1 quantize + pack for gfx950.
 //
 // Layout: one lane owns one group of 16 consecutive weights of a row (32 B of bf16 or 64 B of
 // f32, two or four 16-byte loads); consecutive lanes own consecutive groups, so a wave reads
@@ -324,13 +323,6 @@ __device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
     return *flag == 0;
 }
 
-// Row of a flat group index, gi / gpr, as (gi * M) >> (32 + L) with L = ceil(log2 gpr) and
-// M = ceil(2^(32+L) / gpr) < 2^33: the product stays below 2^64 and the error term, below
-// gi / 2^(32+L) < 2^-(L+1) <= 1/(2 gpr), cannot carry the quotient past an integer (gi < 2^31).
-__device__ __forceinline__ uint32_t div_gpr(uint32_t gi, uint64_t magic, uint32_t shift) {
-    return (uint32_t)(((uint64_t)gi * magic) >> shift);
-}
-
 template <bool BF16, bool WMSE, int NWIN>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
@@ -417,154 +409,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     if (off_out) off_out[gidx] = (int8_t)(best_c - b);
 }
 
-// Quantize + pack at given scale bytes.
-template <bool BF16>
-__global__ __launch_bounds__(kSearchThreads) void k_pack(
-    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, int64_t ldw_bytes,
-    int64_t stride_w_bytes, const uint8_t* __restrict__ scales, const float* __restrict__ S_arr,
-    uint8_t* __restrict__ packed) {
-    const int64_t batch = blockIdx.y;
-    const uint32_t gpr = in >> 4;
-    const uint32_t G = out * gpr;
-    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
-    if (gi >= G) return;
-    const uint32_t row = gi / gpr, g = gi - row * gpr;
-    const int64_t gidx = batch * (int64_t)G + gi;
-    const int c = scales[gidx];
-    float w[16];
-    load_group<BF16>(W + batch * stride_w_bytes + (int64_t)row * ldw_bytes +
-                         (int64_t)g * (BF16 ? 32 : 64),
-                     w);
-    float r = 0.0f;
-    if (c >= 1 && c <= 126) r = __fdiv_rn(1.0f, S_arr[batch] * e4m3_value(c));
-    uint32_t p0 = 0u, p1 = 0u;
-    p0 = e2m1_pack2<0>(p0, w[0] * r, w[1] * r);
-    p0 = e2m1_pack2<1>(p0, w[2] * r, w[3] * r);
-    p0 = e2m1_pack2<2>(p0, w[4] * r, w[5] * r);
-    p0 = e2m1_pack2<3>(p0, w[6] * r, w[7] * r);
-    p1 = e2m1_pack2<0>(p1, w[8] * r, w[9] * r);
-    p1 = e2m1_pack2<1>(p1, w[10] * r, w[11] * r);
-    p1 = e2m1_pack2<2>(p1, w[12] * r, w[13] * r);
-    p1 = e2m1_pack2<3>(p1, w[14] * r, w[15] * r);
-    reinterpret_cast<uint2*>(packed)[gidx] = make_uint2(p0, p1);
-}
-
-// Global scale: S = amax / 2688 (448 * 6) or amax / 1536 (256 * 6), S = 1 if amax = 0.
-// max |w| is taken on binary32 bit patterns of non-negative values (ordered like unsigned
-// integers): exact and independent of order. Pass 1: each workgroup reduces its share (8
-// non-temporal loads of 16 B in flight per lane) to one partial. Pass 2: one workgroup per
-// matrix reduces the partials and writes S.
-constexpr int kAmaxThreads = 256;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-constexpr int kAmaxLoads = 8;
-constexpr int kAmaxMaxBlocks = 1024;
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t absmax_bits(const uint4 d) {
-    if constexpr (BF16) {
-        const uint32_t x[4] = {d.x & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu,
-                               d.w & 0x7FFF7FFFu};
-        uint32_t m = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, max(x[i] << 16, x[i] & 0xFFFF0000u));
-        return m;
-    } else {
-        return max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu),
-                   max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu));
-    }
-}
-
-__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* wmax) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    uint32_t r = wmax[0];
-#pragma unroll
-    for (int i = 1; i < kAmaxThreads / 64; ++i) r = max(r, wmax[i]);
-    return r;
-}
-
-template <bool BF16>
-__global__ __launch_bounds__(kAmaxThreads) void k_amax_partial(const uint8_t* __restrict__ W,
-                                                               int64_t out, int64_t in,
-                                                               int64_t ldw_bytes,
-                                                               int64_t stride_w_bytes,
-                                                               uint32_t* __restrict__ partial) {
-    constexpr int C = BF16 ? 8 : 4;  // elements per 16-byte load
-    __shared__ uint32_t wmax[kAmaxThreads / 64];
-    const int64_t batch = blockIdx.y;
-    const uint8_t* base = W + batch * stride_w_bytes;
-    const int64_t vpr = in / C;
-    const bool dense = ldw_bytes == vpr * 16;
-    const int64_t nvec = out * vpr;
-    const int64_t gsize = (int64_t)gridDim.x * kAmaxThreads;
-    uint32_t m = 0u;
-    for (int64_t v0 = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; v0 < nvec;
-         v0 += kAmaxLoads * gsize) {
-        uint4 d[kAmaxLoads];
-#pragma unroll
-        for (int k = 0; k < kAmaxLoads; ++k) {
-            const int64_t v = v0 + k * gsize;
-            d[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (v < nvec) {
-                const int64_t off = dense ? v * 16 : (v / vpr) * ldw_bytes + (v % vpr) * 16;
-                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
-                d[k] = make_uint4(t.x, t.y, t.z, t.w);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kAmaxLoads; ++k) m = max(m, absmax_bits<BF16>(d[k]));
-    }
-    m = block_max(m, wmax);
-    if (threadIdx.x == 0) partial[batch * gridDim.x + blockIdx.x] = m;
-}
-
-__global__ __launch_bounds__(kAmaxThreads) void k_global_scale_finalize(
-    const uint32_t* __restrict__ partial, int64_t nblk, int rule, float* __restrict__ S) {
-    __shared__ uint32_t wmax[kAmaxThreads / 64];
-    const int64_t batch = blockIdx.x;
-    uint32_t r = 0u;
-    for (int64_t i = threadIdx.x; i < nblk; i += kAmaxThreads)
-        r = max(r, partial[batch * nblk + i]);
-    r = block_max(r, wmax);
-    if (threadIdx.x == 0) {
-        const float amax = __uint_as_float(r);
-        S[batch] = amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
-    }
-}
-
-int64_t amax_blocks(int64_t out, int64_t in) {
-    const int64_t vec = out * (in / 4);  // upper bound on 16-byte loads (f32)
-    const int64_t want = (vec + kAmaxThreads * kAmaxLoads - 1) / (kAmaxThreads * kAmaxLoads);
-    return want < 1 ? 1 : (want > kAmaxMaxBlocks ? kAmaxMaxBlocks : want);
-}
-
 }  // namespace
-
-size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in) {
-    return (size_t)batch * (size_t)amax_blocks(out, in) * sizeof(uint32_t);
-}
-
-hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
-                               int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
-                               hipStream_t stream) {
-    const int64_t nblk = amax_blocks(out, in);
-    uint32_t* partial = static_cast<uint32_t*>(workspace);
-    const int esz = bf16 ? 2 : 4;
-    const dim3 grid((uint32_t)nblk, (uint32_t)batch);
-    if (bf16)
-        hipLaunchKernelGGL(k_amax_partial<true>, grid, dim3(kAmaxThreads), 0, stream,
-                           static_cast<const uint8_t*>(W), out, in, ldw * esz, stride_w * esz,
-                           partial);
-    else
-        hipLaunchKernelGGL(k_amax_partial<false>, grid, dim3(kAmaxThreads), 0, stream,
-                           static_cast<const uint8_t*>(W), out, in, ldw * esz, stride_w * esz,
-                           partial);
-    hipLaunchKernelGGL(k_global_scale_finalize, dim3((uint32_t)batch), dim3(kAmaxThreads), 0,
-                       stream, partial, nblk, rule, S);
-    return hipGetLastError();
-}
 
 hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
@@ -573,9 +418,9 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
                                hipStream_t stream) {
     const int64_t gpr = in / 16;
     const int64_t G = out * gpr;
-    uint32_t L = 0;
-    while (((int64_t)1 << L) < gpr) ++L;
-    const uint64_t magic = (((uint64_t)1 << (32 + L)) + (uint64_t)gpr - 1) / (uint64_t)gpr;
+    uint64_t magic;
+    uint32_t shift;
+    gpr_divisor(gpr, magic, shift);
     const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
     const int esz = bf16 ? 2 : 4;
     const uint8_t* Wb = static_cast<const uint8_t*>(W);
@@ -583,7 +428,7 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
     const int nwin = exhaustive ? 0 : (n == 16 ? 16 : (n == 11 ? 11 : 0));
 #define NVFP4_LAUNCH_SEARCH(B, M, N)                                                              \
     hipLaunchKernelGGL((k_scale_search<B, M, N>), grid, dim3(kSearchThreads), 0, stream, Wb,      \
-                       (uint32_t)out, (uint32_t)in, magic, 32 + L, ldw * esz, stride_w * esz, h,  \
+                       (uint32_t)out, (uint32_t)in, magic, shift, ldw * esz, stride_w * esz, h,  \
                        stride_h, lo, hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset)
 #define NVFP4_LAUNCH_SEARCH_N(B, M)                                                               \
     do {                                                                                          \
@@ -600,23 +445,6 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
     }
 #undef NVFP4_LAUNCH_SEARCH_N
 #undef NVFP4_LAUNCH_SEARCH
-    return hipGetLastError();
-}
-
-hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
-                       int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
-                       uint8_t* packed, hipStream_t stream) {
-    const int64_t G = out * (in / 16);
-    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
-    const int esz = bf16 ? 2 : 4;
-    const uint8_t* Wb = static_cast<const uint8_t*>(W);
-    if (bf16)
-        hipLaunchKernelGGL(k_pack<true>, grid, dim3(kSearchThreads), 0, stream, Wb, (uint32_t)out,
-                           (uint32_t)in, ldw * esz, stride_w * esz, scales, S, packed);
-    else
-        hipLaunchKernelGGL(k_pack<false>, grid, dim3(kSearchThreads), 0, stream, Wb,
-                           (uint32_t)out, (uint32_t)in, ldw * esz, stride_w * esz, scales, S,
-                           packed);
     return hipGetLastError();
 }
 

@@ -205,6 +205,26 @@ def test_pack_parity_and_window_zero(nv):
                                   r["packed"].cpu().numpy())
 
 
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_pack_strided_batched_ragged(nv, dtype):
+    """Pack at given scales on padded rows (ldw > in), a batch of matrices with a gap between
+    them, a group count per row that is not a multiple of the 64 groups a wave covers, and
+    scale bytes over the whole 0..126 range, against the oracle matrix by matrix."""
+    B, out, inp, ldw = 3, 37, 208, 232
+    base = _mat(B * 40, ldw, dtype, seed=81).reshape(B, 40, ldw)
+    W = base[:, :out, :inp]                                     # strided view, gap between matrices
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(82)
+    scales = torch.randint(0, 127, (B, out, inp // 16), generator=g, device=DEV,
+                           dtype=torch.int32).to(torch.uint8)
+    scales[:, 0, :] = torch.arange(inp // 16, device=DEV, dtype=torch.uint8) * 9  # 0, 9, .., 117
+    p = nv.pack(W, scales, S).cpu().numpy()
+    for b in range(B):
+        po = oracle.pack(host_w(W[b]), scales[b].cpu().numpy(), float(S[b].item()))
+        np.testing.assert_array_equal(p[b], po, err_msg=f"matrix {b}")
+
+
 def test_repeatable(nv):
     W = _mat(512, 1024, torch.bfloat16, seed=51)
     h = _h(1024, seed=52)
