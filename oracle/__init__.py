@@ -13,6 +13,9 @@ source. Parity status of each part:
 * E2M1 rounding, E4M3 encode/decode, h, global scale, base code, candidate loss and argmin:
   pinned by the checks in ``tests/test_oracle_*.py`` (closed forms, a library routine,
   exact-rational recomputation, brute force, and the bounds the ScaleSweep page states).
+* Proposal-centred search: pinned by exact-rational recomputation of its candidate list, the
+  reduction to the plain window search (centre = base, no incoming code), the retain-on-tie
+  rule (h = 0) and the no-increase guarantee against the incoming scale.
 * Nibble order inside a byte (low nibble = even element) and the binary32 operation order:
   conventions the pages do not fix. The nibble contents are pinned by a dequantisation round
   trip; the byte order itself is "parity unpinned".
@@ -73,6 +76,9 @@ def _load():
     lib.ref_scale_search.argtypes = [P, I, I64, I64, I64, P, I, I, I, I, ctypes.c_float,
                                      P, P, P, P, I]
     lib.ref_scale_search.restype = I
+    lib.ref_scale_search_proposal.argtypes = [P, I, I64, I64, I64, P, I, I, I, P, P,
+                                              ctypes.c_float, P, P, P, P, I]
+    lib.ref_scale_search_proposal.restype = I
     lib.ref_group_candidates.argtypes = [P, P, ctypes.c_float, I, I, I, P, P]
     lib.ref_group_candidates.restype = I
     lib.ref_pack.argtypes = [P, I, I64, I64, I64, P, ctypes.c_float, P, I]
@@ -177,6 +183,31 @@ def scale_search(W: np.ndarray, h: np.ndarray | None, objective: int, lo: int = 
                                   _ptr(loss), _ptr(offset), threads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle scale_search failed ({rc})")
+    return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def scale_search_proposal(W: np.ndarray, h: np.ndarray | None, objective: int, lo: int, hi: int,
+                          center: np.ndarray, incoming: np.ndarray | None, S: float,
+                          threads: int | None = None):
+    """Proposal-centred search (Replay the Curvature App. D.2): the incoming code (if valid),
+    then clamp(center + o) for o = lo..hi; strict improvement only, so ties keep the incoming
+    code. ``center`` / ``incoming`` are uint8 [out, in/16]. Returns the same dict as
+    ``scale_search`` with offset = c* - clamp(center)."""
+    W = np.ascontiguousarray(W)
+    out, n = W.shape
+    hh = None if h is None else np.ascontiguousarray(h, dtype=np.float32)
+    cen = np.ascontiguousarray(center, dtype=np.uint8).reshape(out, n // 16)
+    inc = None if incoming is None else np.ascontiguousarray(incoming, dtype=np.uint8).reshape(out, n // 16)
+    scales = np.empty((out, n // 16), dtype=np.uint8)
+    packed = np.empty((out, n // 2), dtype=np.uint8)
+    loss = np.empty((out, n // 16), dtype=np.float32)
+    offset = np.empty((out, n // 16), dtype=np.int8)
+    rc = _load().ref_scale_search_proposal(_ptr(W), _dtype_code(W), out, n, n, _ptr(hh), objective,
+                                           lo, hi, _ptr(cen), _ptr(inc), ctypes.c_float(S),
+                                           _ptr(scales), _ptr(packed), _ptr(loss), _ptr(offset),
+                                           threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle scale_search_proposal failed ({rc})")
     return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
 
 

@@ -308,6 +308,108 @@ int ref_scale_search(const void* W, int dtype, int64_t out, int64_t in, int64_t 
     return bad ? REF_ERR_NONFINITE : REF_OK;
 }
 
+/* ------------------------------------------------------------------------------------------ */
+/* Proposal-centred search ([SR] §4.1.3-§4.1.4, App. D.2).                                    */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Schur Replay takes a per-group proposal code, scores the exportable codes within a half-window
+ * around it, and keeps the incoming scale unless a candidate is better ("ten candidates": a
+ * half-window of 4 plus the incoming code; ties are deterministic and the status quo is
+ * retained). Here the candidates are scored with this path's loss (group_loss):
+ *   1. the incoming code, when it is a valid code 1..126;
+ *   2. clamp(center + o, 1, 126) for o = lo..hi ascending, center itself clamped to 1..126.
+ * A candidate replaces the best only when its loss is strictly smaller, so the incoming code
+ * wins every tie and the window's ties go to its lowest code. Without a valid incoming code the
+ * first window candidate starts the scan. An all-zero group gets scale byte 0 as in the plain
+ * search. The offset reported is c* - center. */
+static void search_group_proposal(const float w[16], const float* h, const float* eff,
+                                  const float* rcp, float S, int lo, int hi, int center,
+                                  int incoming, uint8_t* scale, uint8_t nib[16], float* loss,
+                                  int* offset)
+{
+    float a[16];
+    for (int j = 0; j < 16; ++j) a[j] = fabsf(w[j]);
+    if (base_code(a, S) == 0) {
+        *scale = 0;
+        for (int j = 0; j < 16; ++j) nib[j] = (uint8_t)(signbit(w[j]) ? 8 : 0);
+        *loss = 0.0f;
+        *offset = 0;
+        return;
+    }
+    int cen = center < 1 ? 1 : (center > 126 ? 126 : center);
+    int best_c, o0;
+    float best;
+    if (incoming >= 1 && incoming <= 126) {
+        best_c = incoming;
+        best = group_loss(a, h, eff[best_c], rcp[best_c]);
+        o0 = lo;
+    } else {
+        best_c = candidate_code(cen, lo, 0);
+        best = group_loss(a, h, eff[best_c], rcp[best_c]);
+        o0 = lo + 1;
+    }
+    for (int o = o0; o <= hi; ++o) {
+        int c = candidate_code(cen, o, 0);
+        float L = group_loss(a, h, eff[c], rcp[c]);
+        if (L < best) {
+            best = L;
+            best_c = c;
+        }
+    }
+    *scale = (uint8_t)best_c;
+    for (int j = 0; j < 16; ++j) {
+        float x = a[j] * rcp[best_c];
+        nib[j] = (uint8_t)((signbit(w[j]) ? 8 : 0) | ref_e2m1_index(x));
+    }
+    *loss = best;
+    *offset = best_c - cen;
+}
+
+/* Whole matrix, as ref_scale_search, with per-group proposal codes center[out, in/16] and
+ * incoming codes incoming[out, in/16] (NULL: no incoming candidate). */
+int ref_scale_search_proposal(const void* W, int dtype, int64_t out, int64_t in, int64_t ldw,
+                              const float* h, int objective, int lo, int hi,
+                              const uint8_t* center, const uint8_t* incoming, float S,
+                              uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
+                              int nthreads)
+{
+    if (in % 16 != 0 || out < 0 || in < 0 || ldw < in || !center) return REF_ERR_ARG;
+    if (objective == REF_WMSE && !h) return REF_ERR_ARG;
+    if (objective == REF_MSE) h = NULL;
+    if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return REF_ERR_ARG;
+    if (!isfinite(S) || !(S > 0.0f)) return REF_ERR_ARG;
+    float eff[127], rcp[127];
+    if (ref_scale_tables(S, eff, rcp) != REF_OK) return REF_ERR_ARG;
+    if (h)
+        for (int64_t i = 0; i < in; ++i)
+            if (!isfinite(h[i])) return REF_ERR_NONFINITE;
+    int64_t gpr = in / 16;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 4) reduction(| : bad)
+    for (int64_t o = 0; o < out; ++o) {
+        for (int64_t g = 0; g < gpr; ++g) {
+            float w[16];
+            for (int j = 0; j < 16; ++j) {
+                w[j] = load_elem(W, dtype, o * ldw + g * 16 + j);
+                if (!isfinite(w[j])) bad = 1;
+            }
+            int64_t gi = o * gpr + g;
+            uint8_t nib[16], sc;
+            float L;
+            int off;
+            search_group_proposal(w, h ? h + g * 16 : NULL, eff, rcp, S, lo, hi, center[gi],
+                                  incoming ? incoming[gi] : 0, &sc, nib, &L, &off);
+            scales[gi] = sc;
+            for (int k = 0; k < 8; ++k)
+                packed[o * (in / 2) + g * 8 + k] = (uint8_t)(nib[2 * k] | (nib[2 * k + 1] << 4));
+            if (loss) loss[gi] = L;
+            if (offset) offset[gi] = (int8_t)off;
+        }
+    }
+    return bad ? REF_ERR_NONFINITE : REF_OK;
+}
+
 /* Losses of every candidate of one group, in loop order (for checks). Returns the base code;
  * codes[i] / losses[i] for i < count, where count = hi - lo + 1 or 126. */
 int ref_group_candidates(const float w[16], const float* h, float S, int lo, int hi,

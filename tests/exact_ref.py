@@ -85,3 +85,25 @@ def group_exact(w16, h16, S, lo=-9, hi=6, exhaustive=False):
         losses.append(total)
         qidx.append(idxs)
     return {"base": b, "codes": codes, "exact_losses": losses, "q_index": qidx}
+
+
+def losses_at(w16, h16, S, codes):
+    """Exact losses (and E2M1 indices) of one group at the given codes, in the given order."""
+    a = [f32(abs(f32(v))) for v in w16]
+    S = f32(S)
+    losses, qidx = [], []
+    for c in codes:
+        eff = f32(S * f32(float(E4M3[c])))
+        r = f32(f32(1.0) / eff)
+        total = Fraction(0)
+        idxs = []
+        for j in range(16):
+            x = f32(a[j] * r)
+            k = nearest_even(Fraction(float(x)), E2M1)
+            idxs.append(k)
+            d = Fraction(float(a[j])) - E2M1[k] * Fraction(float(eff))
+            weight = Fraction(1) if h16 is None else Fraction(float(f32(h16[j])))
+            total += weight * d * d
+        losses.append(total)
+        qidx.append(idxs)
+    return losses, qidx
