@@ -61,7 +61,9 @@ def kernel_source_hash() -> str:
 
 
 def n_candidates(mode) -> int:
-    return 126 if mode.exhaustive else mode.hi - mode.lo + 1
+    if mode.exhaustive:
+        return 126
+    return mode.hi - mode.lo + 1 + (1 if getattr(mode, "proposal", False) else 0)
 
 
 class Layer:
@@ -105,6 +107,17 @@ class Runner:
         self.ws_s = torch.zeros(max(1, nvfp4.nvfp4_global_scale_workspace_size(E, cfg.out, cfg.inp)),
                                 dtype=torch.uint8, device=dev)
         self.rule = nvfp4.GS_AMAX_256 if cfg.gs_rule == "amax256" else nvfp4.GS_AMAX_448
+        if any(m.proposal for m in cfg.modes):
+            # proposal and incoming codes, made once outside the timed steps: the incoming code is
+            # the max-abs base code, the proposal is the base code moved by a seeded offset
+            from block_scale_search_amd import workloads
+            for s in self.sets:
+                S = nvfp4.global_scale(s.W, self.rule)
+                base = nvfp4.scale_search(s.W, None, S, nvfp4.MSE, 0, 0, with_stats=False)["scales"]
+                off = workloads.proposal_offsets(cfg, base.shape, dev)
+                s.center = (base.to(torch.int32) + off).clamp(1, 126).to(torch.uint8).contiguous()
+                s.incoming = base.contiguous()
+            torch.cuda.synchronize()
 
     def calls(self, s: Layer, aux=None):
         """The step as (label, call, stream_role) triples in issue order; each call is a prepared
@@ -131,6 +144,13 @@ class Runner:
             s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
         for mi, m in enumerate(cfg.modes):
             wm = m.objective == "wmse"
+            if m.proposal:
+                out.append((f"search:{m.label}", nv.nvfp4_scale_search_proposal(
+                    s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
+                    nv.WMSE if wm else nv.MSE, m.lo, m.hi, s.center, s.incoming, s.S,
+                    s.scales[mi], s.packed[mi], prepare=True),
+                    "main_after_h" if wm else "main"))
+                continue
             out.append((f"search:{m.label}", nv.nvfp4_scale_search(
                 s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
                 nv.WMSE if wm else nv.MSE, m.lo, m.hi, m.exhaustive, s.S, s.scales[mi],
@@ -159,55 +179,92 @@ def algorithmic(cfg, label: str):
         return n_w * wb + 4 * cfg.batch, n_w
     mode = next(m for m in cfg.modes if label == f"search:{m.label}")
     bytes_ = n_w * wb + n_w // 2 + n_w // 16 + (cfg.batch * cfg.inp * 4 if mode.objective == "wmse" else 0)
+    if mode.proposal:
+        bytes_ += 2 * (n_w // 16)      # proposal and incoming code per group
     flops = n_w * n_candidates(mode) * FLOPS_PER_ELEM_CAND[mode.objective]
     return bytes_, flops
 
 
-def cpu_baseline(cfg, threads: int):
-    """The oracle, as it stands, over the same workload's first input set (host cores)."""
+def cpu_baseline(cfg, layer, threads: int):
+    """The oracle, as it stands, on a bounded sample of the first input set (the GPU's own
+    inputs, copied to the host), projected to the whole step.
+
+    Sample: up to 2^24 weights (whole rows, or whole experts of a batch) and the tokens that feed
+    them (the first chunk, or the sampled experts' segments). Passes are repeated until at least
+    10 s of wall time. Projection: the h time scales with the step's tokens over the sampled
+    tokens, the global-scale and search time with the step's weights over the sampled weights.
+    """
     import numpy as np
     import torch
 
     import oracle
-    from block_scale_search_amd import workloads
 
-    def bits(t):
-        t = t.cpu()
+    def host(t):
+        t = t.detach().cpu().contiguous()
         return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
-    W = bits(workloads.make_weights(cfg, "cpu"))
-    sigma = workloads.make_sigma(cfg, "cpu")
-    Xs = [bits(workloads.make_activation_chunk(cfg, sigma, c, "cpu")[0])
-          for c in range(workloads.n_chunks(cfg))]
-    rows = W.shape[-2]
-    if cfg.batch > 1 or rows * cfg.inp > (1 << 26):
-        raise SystemExit("cpu baseline is sized for single-matrix workloads up to 64M weights")
-    def one_pass():
-        acc = None
-        for X in Xs:
-            acc, h = oracle.diag_hessian(X, acc, threads=threads)
-        S = oracle.global_scale(W, oracle.GS_AMAX_256 if cfg.gs_rule == "amax256"
-                                else oracle.GS_AMAX_448)
-        for m in cfg.modes:
-            oracle.scale_search(W, h if m.objective == "wmse" else None,
-                                oracle.WMSE if m.objective == "wmse" else oracle.MSE, m.lo, m.hi,
-                                m.exhaustive, S, threads=threads)
+    budget = 1 << 24
+    S_all = layer.S.cpu().numpy().reshape(-1)
+    center = incoming = None
+    if cfg.batch == 1:
+        R = max(1, min(cfg.out, budget // cfg.inp))
+        Ws = [host(layer.W[:R])]
+        if hasattr(layer, "center"):
+            center, incoming = layer.center[:R].cpu().numpy(), layer.incoming[:R].cpu().numpy()
+        Xs = [host(layer.chunks[0])]
+        Ss = [float(S_all[0])]
+        w_frac = cfg.out / R
+        tok_sample = layer.chunks[0].shape[0]
+        desc = f"{R} of {cfg.out} rows"
+    else:
+        E = max(1, min(cfg.batch, budget // (cfg.out * cfg.inp)))
+        Ws = [host(layer.W[e]) for e in range(E)]
+        seg = layer.seg.cpu().numpy()
+        Xs = [host(layer.chunks[0][int(seg[e]):int(seg[e + 1])]) for e in range(E)]
+        Ss = [float(S_all[e]) for e in range(E)]
+        w_frac = cfg.batch / E
+        tok_sample = int(seg[E])
+        desc = f"{E} of {cfg.batch} experts"
+    tok_frac = cfg.tokens / max(1, tok_sample)
+    rule = oracle.GS_AMAX_256 if cfg.gs_rule == "amax256" else oracle.GS_AMAX_448
+    mats = list(zip(Ws, Xs, Ss))
 
-    # whole passes until at least 10 s of wall time (at least one pass)
-    t0 = time.perf_counter()
+    t_h = t_s = 0.0
     passes = 0
+    t0 = time.perf_counter()
     while True:
-        one_pass()
+        for W, X, S in mats:
+            a = time.perf_counter()
+            if cfg.batch == 1:
+                acc = None
+                acc, h = oracle.diag_hessian(X, acc, threads=threads)
+            else:
+                acc, h = oracle.diag_hessian(X, None, threads=threads)
+            b = time.perf_counter()
+            oracle.global_scale(W, rule)
+            for m in cfg.modes:
+                wm = m.objective == "wmse"
+                if m.proposal:
+                    oracle.scale_search_proposal(W, h if wm else None,
+                                                 oracle.WMSE if wm else oracle.MSE, m.lo, m.hi,
+                                                 center, incoming, S, threads=threads)
+                else:
+                    oracle.scale_search(W, h if wm else None, oracle.WMSE if wm else oracle.MSE,
+                                        m.lo, m.hi, m.exhaustive, S, threads=threads)
+            c = time.perf_counter()
+            t_h += b - a
+            t_s += c - b
         passes += 1
-        dt = time.perf_counter() - t0
-        if dt >= 10.0:
+        if time.perf_counter() - t0 >= 10.0:
             break
-    searched = cfg.n_weights * len(cfg.modes) * passes
-    return {"value": searched / dt, "unit": "weights/s", "cores": threads, "kind": "oracle",
-            "sample": f"the whole {cfg.name} workload (first input set) {passes} times: h over "
-                      f"{cfg.tokens}x{cfg.inp} tokens, global scale, "
-                      f"{' + '.join(m.label for m in cfg.modes)} over {cfg.out}x{cfg.inp} "
-                      f"weights; {dt:.2f} s wall on {threads} threads"}
+    step_s = (t_h * tok_frac + t_s * w_frac) / passes
+    searched = cfg.n_weights * len(cfg.modes)
+    return {"value": searched / step_s, "unit": "weights/s", "cores": threads, "kind": "oracle",
+            "sample": f"first input set: {desc} and {tok_sample} of {cfg.tokens} tokens, "
+                      f"h + global scale + {' + '.join(m.label for m in cfg.modes)}, "
+                      f"{passes} passes in {time.perf_counter() - t0:.1f} s on {threads} threads; "
+                      f"projected to the whole step (h time x {tok_frac:.3g}, "
+                      f"search time x {w_frac:.3g})"}
 
 
 def read_traffic(workload: str, kernel_label: str):
@@ -383,11 +440,7 @@ def main():
     cpu = None
     if not args.no_cpu:
         threads = min(16, len(os.sched_getaffinity(0)))
-        try:
-            cpu = cpu_baseline(cfg, threads)
-        except SystemExit as e:
-            cpu = {"value": None, "unit": "weights/s", "cores": 0, "kind": "oracle",
-                   "sample": str(e)}
+        cpu = cpu_baseline(cfg, runner.sets[0], threads)
 
     searched = cfg.n_weights * len(cfg.modes)
     line = {

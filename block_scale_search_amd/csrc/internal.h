@@ -29,10 +29,13 @@ hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t 
                                int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
                                hipStream_t stream);
 
+// center == NULL: plain window (around the base code) or exhaustive search. center != NULL:
+// window around center[] with the optional incoming[] code kept on ties (exhaustive false).
 hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
                                bool wmse, int lo, int hi, bool exhaustive, const float* S,
                                uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
+                               const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream);
 
 hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,

@@ -323,12 +323,15 @@ __device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
     return *flag == 0;
 }
 
-template <bool BF16, bool WMSE, int NWIN>
+// PROPOSAL: the window is centred on a per-group proposal code center[] instead of the base
+// code, and a valid incoming code incoming[] (if given) is scored as well and kept on ties.
+template <bool BF16, bool WMSE, int NWIN, bool PROPOSAL>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
     uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h,
     int lo, int hi, int exhaustive, const float* __restrict__ S_arr, uint8_t* __restrict__ scales,
-    uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out) {
+    uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out,
+    const uint8_t* __restrict__ center, const uint8_t* __restrict__ incoming) {
     __shared__ float2 tab[128];
     __shared__ int flag;
     const int64_t batch = blockIdx.y;
@@ -374,15 +377,35 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
         b = max(e4m3_rne_sat(s_star), 1);
     }
     const bool live = valid && b > 0;
+    const int64_t gidx = batch * (int64_t)G + gi;
+
+    // window centre: the base code, or the group's proposal code clamped to 1..126
+    int cen = b;
+    int inc = 0;
+    if constexpr (PROPOSAL) {
+        cen = valid ? min(max((int)center[gidx], 1), 126) : 1;
+        inc = (valid && incoming) ? (int)incoming[gidx] : 0;
+    }
 
     // The running best starts at +inf with the first candidate's code, so a group whose every
     // loss overflows keeps its first candidate, as the ascending scan does.
     float best = __builtin_inff();
-    int best_c = exhaustive ? 1 : min(max(b + lo, 1), 126);
+    int best_c = exhaustive ? 1 : min(max(cen + lo, 1), 126);
     if (exhaustive) {
         if (__any(live)) search_all<WMSE>(w, h, tab, octave_ok, live, b, best, best_c);
     } else {
-        search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, b + lo, hi - lo + 1, best, best_c);
+        search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, cen + lo, hi - lo + 1, best, best_c);
+    }
+    if constexpr (PROPOSAL) {
+        // the incoming code comes first in the scan order, so it wins every tie
+        if (live && inc >= 1 && inc <= 126) {
+            const float2 er = tab[inc];
+            const float L = loss_one<WMSE>(w, h, er.x, er.y);
+            if (!(best < L)) {
+                best = L;
+                best_c = inc;
+            }
+        }
     }
     if (!live) {
         best = 0.0f;
@@ -402,11 +425,10 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     p1 = e2m1_pack2<1>(p1, w[10] * r, w[11] * r);
     p1 = e2m1_pack2<2>(p1, w[12] * r, w[13] * r);
     p1 = e2m1_pack2<3>(p1, w[14] * r, w[15] * r);
-    const int64_t gidx = batch * (int64_t)G + gi;
     reinterpret_cast<uint2*>(packed)[gidx] = make_uint2(p0, p1);
     scales[gidx] = (uint8_t)best_c;
     if (loss_out) loss_out[gidx] = best;
-    if (off_out) off_out[gidx] = (int8_t)(best_c - b);
+    if (off_out) off_out[gidx] = (int8_t)(live ? best_c - cen : 0);
 }
 
 }  // namespace
@@ -415,6 +437,7 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
                                int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
                                bool wmse, int lo, int hi, bool exhaustive, const float* S,
                                uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
+                               const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream) {
     const int64_t gpr = in / 16;
     const int64_t G = out * gpr;
@@ -425,16 +448,23 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
     const int esz = bf16 ? 2 : 4;
     const uint8_t* Wb = static_cast<const uint8_t*>(W);
     const int n = hi - lo + 1;
-    const int nwin = exhaustive ? 0 : (n == 16 ? 16 : (n == 11 ? 11 : 0));
-#define NVFP4_LAUNCH_SEARCH(B, M, N)                                                              \
-    hipLaunchKernelGGL((k_scale_search<B, M, N>), grid, dim3(kSearchThreads), 0, stream, Wb,      \
-                       (uint32_t)out, (uint32_t)in, magic, shift, ldw * esz, stride_w * esz, h,  \
-                       stride_h, lo, hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset)
+    const bool proposal = center != nullptr;
+    // windows with a compile-time length: 16 and 11 (the pages' windows), 9 (a half-window of 4
+    // around a proposal)
+    const int nwin = exhaustive ? 0 : (n == 16 || n == 11 || n == 9 ? n : 0);
+#define NVFP4_LAUNCH_SEARCH(B, M, N, P)                                                           \
+    hipLaunchKernelGGL((k_scale_search<B, M, N, P>), grid, dim3(kSearchThreads), 0, stream, Wb,   \
+                       (uint32_t)out, (uint32_t)in, magic, shift, ldw * esz, stride_w * esz, h,   \
+                       stride_h, lo, hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset,     \
+                       center, incoming)
 #define NVFP4_LAUNCH_SEARCH_N(B, M)                                                               \
     do {                                                                                          \
-        if (nwin == 16) NVFP4_LAUNCH_SEARCH(B, M, 16);                                            \
-        else if (nwin == 11) NVFP4_LAUNCH_SEARCH(B, M, 11);                                       \
-        else NVFP4_LAUNCH_SEARCH(B, M, 0);                                                        \
+        if (proposal) {                                                                           \
+            if (nwin == 9) NVFP4_LAUNCH_SEARCH(B, M, 9, true);                                    \
+            else NVFP4_LAUNCH_SEARCH(B, M, 0, true);                                              \
+        } else if (nwin == 16) NVFP4_LAUNCH_SEARCH(B, M, 16, false);                              \
+        else if (nwin == 11) NVFP4_LAUNCH_SEARCH(B, M, 11, false);                                \
+        else NVFP4_LAUNCH_SEARCH(B, M, 0, false);                                                 \
     } while (0)
     if (bf16) {
         if (wmse) NVFP4_LAUNCH_SEARCH_N(true, true);

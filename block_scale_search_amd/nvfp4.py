@@ -39,6 +39,8 @@ _SIGS = {
     "nvfp4_global_scale": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
     "nvfp4_scale_search": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I, _I32, _I32, _I,
                             _P, _P, _P, _P, _P, _P], _I),
+    "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
+                                     _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -168,6 +170,29 @@ def nvfp4_scale_search(W, batch, out, inp, ldw, stride_w, group_size, h, stride_
         _dev(offset, "offset", (torch.int8,)), _stream(stream)), prepare)
 
 
+def nvfp4_scale_search_proposal(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h,
+                                objective, lo, hi, center, incoming, S, scales, packed, loss=None,
+                                offset=None, stream=None, prepare=False):
+    G = batch * out * (inp // 16)
+    _need(scales, G, "scales")
+    _need(packed, G * 8, "packed")
+    _need(center, G, "center")
+    if incoming is not None:
+        _need(incoming, G, "incoming")
+    _need(S, batch, "S")
+    if loss is not None:
+        _need(loss, G, "loss")
+    if offset is not None:
+        _need(offset, G, "offset")
+    return _run("nvfp4_scale_search_proposal", (
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        group_size, _dev(h, "h", (torch.float32,)), stride_h, objective, lo, hi,
+        _dev(center, "center", (torch.uint8,)), _dev(incoming, "incoming", (torch.uint8,)),
+        _dev(S, "S", (torch.float32,)), _dev(scales, "scales", (torch.uint8,)),
+        _dev(packed, "packed", (torch.uint8,)), _dev(loss, "loss", (torch.float32,)),
+        _dev(offset, "offset", (torch.int8,)), _stream(stream)), prepare)
+
+
 def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None, prepare=False):
     G = batch * out * (inp // 16)
     _need(scales, G, "scales")
@@ -250,6 +275,32 @@ def scale_search(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objec
         stride_h = h.stride(0) if h.dim() == 2 else 0
     nvfp4_scale_search(W, b, o, n, ldw, sw, 16, h if objective == WMSE else None, stride_h,
                        objective, lo, hi, exhaustive, S, scales, packed, loss, offset, stream)
+    return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def scale_search_proposal(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objective: int,
+                          center: torch.Tensor, incoming: torch.Tensor | None = None,
+                          lo: int = -4, hi: int = 4, with_stats: bool = True, stream=None):
+    """Proposal-centred search + pack: window lo..hi around center[...] (uint8, shaped like the
+    scales), the incoming codes (or None) scored first and kept on ties."""
+    b, o, n, ldw, sw = _bmat(W)
+    shp = (o, n // 16) if W.dim() == 2 else (b, o, n // 16)
+    dev = W.device
+    scales = torch.empty(shp, dtype=torch.uint8, device=dev)
+    packed = torch.empty(shp[:-1] + (n // 2,), dtype=torch.uint8, device=dev)
+    loss = torch.empty(shp, dtype=torch.float32, device=dev) if with_stats else None
+    offset = torch.empty(shp, dtype=torch.int8, device=dev) if with_stats else None
+    stride_h = 0
+    if objective == WMSE:
+        if h is None:
+            raise ValueError("WMSE needs h")
+        stride_h = h.stride(0) if h.dim() == 2 else 0
+    for name, t in (("center", center), ("incoming", incoming)):
+        if t is not None and (tuple(t.shape) != shp or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous uint8 tensor of shape {shp}")
+    nvfp4_scale_search_proposal(W, b, o, n, ldw, sw, 16, h if objective == WMSE else None,
+                                stride_h, objective, lo, hi, center, incoming, S, scales, packed,
+                                loss, offset, stream)
     return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
 
 

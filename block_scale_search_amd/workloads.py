@@ -14,6 +14,7 @@ Schur Replay: a 255-document set). Synthetic tensors of the layer shapes below s
                                                                per-expert channel std e^N(0,1)
   mlp70b   W 28672x8192 and 8192x28672 bf16, 0.015*t(5);       X 65536x{8192, 28672}, std e^(1.5 N),
                                                                streamed in 8192-token chunks
+  mlp70b_up_proposal  the 70B up/gate layer with proposal codes = base codes + U{-3..3}
 
 Every tensor is drawn as float32 from a torch.Generator seeded per (config, stream) and then
 rounded to bf16 (round-to-nearest-even) where the config says bf16. Student-t variates are
@@ -30,7 +31,7 @@ import numpy as np
 import torch
 
 # stream ids: one independent generator per (config seed, stream)
-_W, _OUT, _SIGMA, _X, _ZIPF = 1, 2, 3, 4, 5
+_W, _OUT, _SIGMA, _X, _ZIPF, _PROP = 1, 2, 3, 4, 5, 6
 
 
 def _gen(seed: int, stream: int, device) -> torch.Generator:
@@ -116,11 +117,14 @@ class Mode:
     lo: int = 0
     hi: int = 0
     exhaustive: bool = False
+    proposal: bool = False    # window around per-group proposal codes, plus the incoming code
 
     @property
     def label(self) -> str:
         if self.exhaustive:
             return f"{self.objective.upper()} exhaustive(126)"
+        if self.proposal:
+            return f"{self.objective.upper()} proposal [{self.lo},{self.hi}] + incoming"
         return f"{self.objective.upper()} [{self.lo},{self.hi}]"
 
 
@@ -162,7 +166,23 @@ CONFIGS = {
     "mlp70b_down": Config("mlp70b_down", 1005, 1, 8192, 28672, 65536, torch.bfloat16, "amax448",
                           [Mode("wmse", -9, 6), Mode("wmse", exhaustive=True)], chunk_tokens=8192,
                           description="70B-shaped MLP down: W 8192x28672, X 65536x28672"),
+    # The proposal-centred variant of Replay the Curvature (App. D.2: half-window 4 plus the
+    # incoming scale) on the 70B up-projection shape. The proposal codes are the max-abs base
+    # codes moved by seeded offsets in [-3, 3] (proposal_offsets); the incoming codes are the
+    # base codes (the status-quo scale before refinement).
+    "mlp70b_up_proposal": Config("mlp70b_up_proposal", 1004, 1, 28672, 8192, 65536,
+                                 torch.bfloat16, "amax448", [Mode("wmse", -4, 4, proposal=True)],
+                                 chunk_tokens=8192,
+                                 description="70B-shaped MLP up/gate, proposal-centred window "
+                                             "[-4,4] + incoming scale: W 28672x8192, X 65536x8192"),
 }
+
+
+def proposal_offsets(cfg: Config, shape, device="cpu"):
+    """Seeded integer offsets in [-3, 3] that move a group's base code to a synthetic proposal
+    (the pages' proposals come from a GPTQ-state quadratic fit that needs trained weights)."""
+    g = _gen(cfg.seed, _PROP, device)
+    return torch.randint(-3, 4, tuple(shape), generator=g, device=device, dtype=torch.int32)
 
 
 def make_weights(cfg: Config, device="cpu"):

@@ -158,6 +158,34 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
                                 uint8_t* packed, float* loss, int8_t* offset, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Steps 3-4 with a proposal-centred window and the incoming scale kept on ties ([SR] §4.1.3 and
+ * §4.1.4: a proposal gives a neighbourhood of exportable scales that is then scored, and keeping
+ * the status-quo scale means the local search cannot increase the loss; [SR] App. D.2: a
+ * half-window of 4 plus the incoming exportable scale, ten candidates in all; deterministic ties).
+ *
+ * Same arithmetic, arguments and outputs as nvfp4_scale_search, with these differences:
+ *   centre  = center[b, o, g] clamped to 1..126 (replaces the base code as the window centre)
+ *   scan    = incoming[b, o, g] first when incoming != NULL and the code is 1..126, then
+ *             clamp(centre + o, 1, 126) for o = lo..hi ascending; a candidate replaces the best
+ *             only when its loss is strictly smaller, so the incoming code wins every tie and the
+ *             window's ties go to its lowest code
+ *   offset[b, o, g] = choice - centre
+ * An all-zero group still gets scale byte 0, zero codes, loss 0 and offset 0.
+ *
+ * center    device, uint8 [batch, out, in/16], required.
+ * incoming  device, uint8 [batch, out, in/16], or NULL for no incoming candidate; codes outside
+ *           1..126 mean "no incoming candidate" for that group.
+ * lo, hi    window offsets around the centre, -125 <= lo <= 0 <= hi <= 125 (no exhaustive mode).
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_scale_search_proposal(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                         int64_t in, int64_t ldw, int64_t stride_w,
+                                         int32_t group_size, const float* h, int64_t stride_h,
+                                         int objective, int32_t lo, int32_t hi,
+                                         const uint8_t* center, const uint8_t* incoming,
+                                         const float* S, uint8_t* scales, uint8_t* packed,
+                                         float* loss, int8_t* offset, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Quantize + pack at given scale bytes ([HS] App. B: the group is quantized once with its
  * scale; round-to-nearest at a fixed scale). Same layouts and nibble rule as above; a scale
  * byte of 0 gives signed zero codes. Scale bytes must be 0..126.

@@ -313,8 +313,8 @@ int ref_scale_search(const void* W, int dtype, int64_t out, int64_t in, int64_t 
 /* ------------------------------------------------------------------------------------------ */
 
 /* Schur Replay takes a per-group proposal code, scores the exportable codes within a half-window
- * around it, and keeps the incoming scale unless a candidate is better ("ten candidates": a
- * half-window of 4 plus the incoming code; ties are deterministic and the status quo is
+ * around it, and keeps the incoming scale unless a candidate is better (ten candidates in
+ * all: a half-window of 4 plus the incoming code; ties are deterministic and the status quo is
  * retained). Here the candidates are scored with this path's loss (group_loss):
  *   1. the incoming code, when it is a valid code 1..126;
  *   2. clamp(center + o, 1, 126) for o = lo..hi ascending, center itself clamped to 1..126.

@@ -22,7 +22,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("nvfp4_diag_hessian", "nvfp4_diag_hessian_batched", "nvfp4_global_scale",
-                 "nvfp4_scale_search", "nvfp4_pack", "nvfp4_status_string",
+                 "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
+                 "nvfp4_status_string",
                  "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
         assert want in names
 
@@ -85,6 +86,31 @@ def test_scale_search_rejects_bad_arguments(lib):
     assert _search(lib, inp=0, ldw=0) == n.OK
     # an exhaustive search ignores the window
     assert _search(lib, exh=1, lo=5, hi=-5, W=None) == n.ERR_NULL
+
+
+def _proposal(lib, **kw):
+    a = dict(W=FAKE, dt=1, batch=1, out=4, inp=64, ldw=64, sw=256, gs=16, h=FAKE, sh=0, obj=1,
+             lo=-4, hi=4, cen=FAKE, inc=None, S=FAKE, sc=FAKE, pk=FAKE, loss=None, off=None)
+    a.update(kw)
+    return lib.nvfp4_scale_search_proposal(a["W"], a["dt"], a["batch"], a["out"], a["inp"],
+                                           a["ldw"], a["sw"], a["gs"], a["h"], a["sh"], a["obj"],
+                                           a["lo"], a["hi"], a["cen"], a["inc"], a["S"], a["sc"],
+                                           a["pk"], a["loss"], a["off"], None)
+
+
+def test_scale_search_proposal_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    assert _proposal(lib, gs=8) == n.ERR_ARG
+    assert _proposal(lib, obj=2) == n.ERR_ARG
+    assert _proposal(lib, lo=1) == n.ERR_WINDOW
+    assert _proposal(lib, hi=-2) == n.ERR_WINDOW
+    assert _proposal(lib, lo=-126) == n.ERR_WINDOW
+    assert _proposal(lib, cen=None) == n.ERR_NULL                 # the proposal is required
+    assert _proposal(lib, h=None) == n.ERR_NULL
+    assert _proposal(lib, W=ODD) == n.ERR_ALIGN
+    assert _proposal(lib, dt=3) == n.ERR_DTYPE
+    assert _proposal(lib, inp=40, ldw=40) == n.ERR_SHAPE
+    assert _proposal(lib, out=0, cen=None) == n.OK                # empty: nothing enqueued
 
 
 def test_pack_and_global_scale_reject_bad_arguments(lib):
