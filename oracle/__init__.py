@@ -13,6 +13,10 @@ source. Parity status of each part:
 * E2M1 rounding, E4M3 encode/decode, h, global scale, base code, candidate loss and argmin:
   pinned by the checks in ``tests/test_oracle_*.py`` (closed forms, a library routine,
   exact-rational recomputation, brute force, and the bounds the ScaleSweep page states).
+* Dequantisation and the layer-output error: pinned by the closed forms in
+  ``tests/test_oracle_output_error.py`` (quantised weights give zero error, identity
+  activations give the squared residual norm, scaling X by 2 multiplies by 4) and brute force
+  in exact rationals on a tiny layer.
 * Proposal-centred search: pinned by exact-rational recomputation of its candidate list, the
   reduction to the plain window search (centre = base, no incoming code), the retain-on-tie
   rule (h = 0) and the no-increase guarantee against the incoming scale.
@@ -79,6 +83,8 @@ def _load():
     lib.ref_scale_search_proposal.argtypes = [P, I, I64, I64, I64, P, I, I, I, P, P,
                                               ctypes.c_float, P, P, P, P, I]
     lib.ref_scale_search_proposal.restype = I
+    lib.ref_dequant.argtypes = [P, P, I64, I64, ctypes.c_float, P]
+    lib.ref_dequant.restype = I
     lib.ref_group_candidates.argtypes = [P, P, ctypes.c_float, I, I, I, P, P]
     lib.ref_group_candidates.restype = I
     lib.ref_pack.argtypes = [P, I, I64, I64, I64, P, ctypes.c_float, P, I]
@@ -235,6 +241,37 @@ def pack(W: np.ndarray, scales: np.ndarray, S: float, threads: int | None = None
     if rc != 0:
         raise ValueError(f"oracle pack failed ({rc})")
     return packed
+
+
+def dequant(packed: np.ndarray, scales: np.ndarray, S: float) -> np.ndarray:
+    """Binary32 dequantised weights [out, in] from packed codes [out, in/2] and scales."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    out, half = packed.shape
+    w_hat = np.empty((out, 2 * half), dtype=np.float32)
+    rc = _load().ref_dequant(_ptr(packed), _ptr(scales), out, 2 * half, ctypes.c_float(S),
+                             _ptr(w_hat))
+    if rc != 0:
+        raise ValueError(f"oracle dequant failed ({rc})")
+    return w_hat
+
+
+def output_error(X: np.ndarray, W: np.ndarray, packed: np.ndarray, scales: np.ndarray,
+                 S: float) -> np.ndarray:
+    """Per-output-row layer-output error err[o] = sum_t (sum_i x_ti (w_oi - w_hat_oi))^2
+    (H-Scale §3: the quantised layer's output against the original's on calibration inputs).
+
+    Everything in binary64: x and w are exact in binary64, w_hat is the binary32 dequantised
+    weight, the residual w - w_hat is exact in binary64, and the product is a binary64 matmul
+    (a library primitive as one step), then the squares are summed over tokens."""
+    def f64(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:            # bf16 bit patterns
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+    E = f64(W) - dequant(packed, scales, S).astype(np.float64)
+    Y = f64(X) @ E.T
+    return (Y * Y).sum(axis=0)
 
 
 def unpack_nibbles(packed: np.ndarray) -> np.ndarray:

@@ -460,6 +460,35 @@ int ref_pack(const void* W, int dtype, int64_t out, int64_t in, int64_t ldw,
     return bad ? REF_ERR_ARG : REF_OK;
 }
 
+/* ------------------------------------------------------------------------------------------ */
+/* Layer-output evaluation ([HS] §3: layer-output reconstruction; the activation-loss         */
+/* comparison of Min-Max, MSE-guided and Hessian-guided scales).                             */
+/* ------------------------------------------------------------------------------------------ */
+
+/* Dequantised weights: w_hat[o, i] = sign * level * eff[c] in binary32 (one rounding of the
+ * product level * eff, with eff = fl(S * dec(c))), from packed codes [out, in/2] (element 2k in
+ * the low nibble of byte k) and scale bytes [out, in/16]. Scale byte 0 gives signed zeros.
+ * Scale bytes above 126 are refused. */
+int ref_dequant(const uint8_t* packed, const uint8_t* scales, int64_t out, int64_t in, float S,
+                float* w_hat)
+{
+    if (in % 16 != 0 || out < 0 || in < 0) return REF_ERR_ARG;
+    if (!isfinite(S) || !(S > 0.0f)) return REF_ERR_ARG;
+    float eff[127], rcp[127];
+    if (ref_scale_tables(S, eff, rcp) != REF_OK) return REF_ERR_ARG;
+    int64_t gpr = in / 16;
+    for (int64_t o = 0; o < out; ++o)
+        for (int64_t i = 0; i < in; ++i) {
+            int c = scales[o * gpr + i / 16];
+            if (c > 126) return REF_ERR_ARG;
+            uint8_t byte = packed[o * (in / 2) + i / 2];
+            int nib = (i & 1) ? (byte >> 4) : (byte & 15);
+            float mag = (c == 0) ? 0.0f : E2M1_LEVEL[nib & 7] * eff[c];
+            w_hat[o * in + i] = (nib & 8) ? -mag : mag;
+        }
+    return REF_OK;
+}
+
 /* Batch helper for many scalar E2M1 / E4M3 decisions (used by the format checks). */
 void ref_e2m1_index_many(const float* x, int64_t n, uint8_t* out)
 {
