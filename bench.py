@@ -39,6 +39,8 @@ HBM_PEAK_GBS = 8000.0
 # instructions, which this build does not emit; 78.6 TFLOP/s is the unpacked fma rate.
 VALU_PEAK_TOPS = 39.32
 VALU_PEAK_TFLOPS = 78.6
+# dense bf16 MFMA peak of MI355X (published, no sparsity)
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 VALU_PUBLISHED_TFLOPS = 157.3
 # algorithmic fp32 operations per element and candidate, one VALU lane-operation each: the
 # multiply x = |w| * r, the E2M1 rounding of x, the residual fma, the accumulating fma, and for
@@ -293,6 +295,9 @@ def main():
                     help="record per-call HIP events on every Nth timed step (1 = all)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--output-error", action="store_true",
+                    help="also time the layer-output error evaluation (MFMA) of the last mode's "
+                         "codes over the first token chunk, outside the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU split is "
@@ -388,6 +393,37 @@ def main():
     torch.cuda.synchronize()
     pack_us = p0.elapsed_time(p1) * 1e3 / reps
 
+    # layer-output error (evaluation, outside the step): X chunk 0 against W and the last
+    # mode's codes of each input set
+    oe = None
+    if args.output_error and cfg.batch == 1:
+        T0 = runner.sets[0].chunks[0].shape[0]
+        ws_oe = torch.empty(nv.nvfp4_output_error_workspace_size(T0, cfg.out, cfg.inp),
+                            dtype=torch.uint8, device=dev)
+        errs = [torch.empty(cfg.out, dtype=torch.float64, device=dev) for _ in runner.sets]
+        calls_oe = [nv.nvfp4_output_error(s_.chunks[0], T0, cfg.inp, cfg.inp, s_.W, cfg.out,
+                                          cfg.inp, s_.scales[-1], s_.packed[-1], s_.S, e_, False,
+                                          ws_oe, prepare=True)
+                    for s_, e_ in zip(runner.sets, errs)]
+        for f in calls_oe:
+            f()
+        torch.cuda.synchronize()
+        reps_oe = max(2 * n_sets, 10)
+        p0.record(main)
+        for i in range(reps_oe):
+            calls_oe[i % n_sets]()
+        p1.record(main)
+        torch.cuda.synchronize()
+        oe_us = p0.elapsed_time(p1) * 1e3 / reps_oe
+        flops = 2.0 * T0 * cfg.inp * cfg.out
+        oe = {"avg_us": round(oe_us, 2), "tokens": T0, "alg_flops": flops,
+              "TFLOP/s": round(flops / oe_us / 1e6, 1),
+              "frac_mfma_bf16_2500": round(flops / oe_us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4),
+              "mfma_flops_issued": 2 * flops,
+              "note": "E = W - W_hat runs as bf16 E_hi + E_lo, so the MFMAs issue twice the "
+                      "algorithmic flops; the time includes the residual split and the "
+                      "reduction kernels"}
+
     per_label = {}
     for row in ev:
         for lab, (e0, e1) in zip(labels, row):
@@ -465,6 +501,8 @@ def main():
         "kernels": kernels,
         "h_reduce_GB/s": kernels["h_reduce"]["GB/s"],
     }
+    if oe is not None:
+        line["output_error"] = oe
     print(json.dumps(line), flush=True)
 
 

@@ -202,4 +202,40 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
                                          static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in) {
+    if (tokens < 0 || out < 0 || in < 0) return 0;
+    return nvfp4::output_error_workspace_bytes(tokens, out, in);
+}
+
+nvfp4_status nvfp4_output_error(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                int64_t ldx, const void* W, int w_dtype, int64_t out, int64_t ldw,
+                                const uint8_t* scales, const uint8_t* packed, const float* S,
+                                double* err, int accumulate, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    if (x_dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    if (st != NVFP4_OK) return st;
+    if (tokens < 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    if ((tokens + 127) / 128 > 65535) return NVFP4_ERR_SHAPE;
+    if (out == 0) return NVFP4_OK;
+    if (err == nullptr) return NVFP4_ERR_NULL;
+    if (reinterpret_cast<uintptr_t>(err) & 7u) return NVFP4_ERR_ALIGN;
+    // with no tokens or no columns there are no terms: the kernels then only write err
+    // (0, or its old value when accumulating) and read nothing else
+    if (tokens > 0 && in > 0) {
+        if (X == nullptr || scales == nullptr || packed == nullptr || S == nullptr)
+            return NVFP4_ERR_NULL;
+        if (!aligned16(X) || (reinterpret_cast<uintptr_t>(packed) & 3u) ||
+            (reinterpret_cast<uintptr_t>(S) & 3u))
+            return NVFP4_ERR_ALIGN;
+    }
+    const size_t need = nvfp4::output_error_workspace_bytes(tokens, out, in);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_output_error(X, tokens, in, ldx, W,
+                                                 w_dtype == NVFP4_DTYPE_BF16, out, ldw, scales,
+                                                 packed, S, err, accumulate != 0, workspace,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -38,6 +38,13 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
                                const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream);
 
+// Layer-output error: workspace bytes (residual halves + token-tile partials) and launch.
+size_t output_error_workspace_bytes(int64_t tokens, int64_t out, int64_t in);
+hipError_t launch_output_error(const void* X, int64_t tokens, int64_t in, int64_t ldx,
+                               const void* W, bool w_bf16, int64_t out, int64_t ldw,
+                               const uint8_t* scales, const uint8_t* packed, const float* S,
+                               double* err, bool accumulate, void* workspace, hipStream_t stream);
+
 hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                        int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
                        uint8_t* packed, hipStream_t stream);

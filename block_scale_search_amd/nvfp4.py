@@ -42,6 +42,9 @@ _SIGS = {
     "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
                                      _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
+    "nvfp4_output_error_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "nvfp4_output_error": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _I64, _P, _P, _P, _P, _I,
+                            _P, _SZ, _P], _I),
 }
 for _name, (_args, _res) in _SIGS.items():
     _f = getattr(_lib, _name)
@@ -203,6 +206,22 @@ def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None
         _dev(packed, "packed", (torch.uint8,)), _stream(stream)), prepare)
 
 
+def nvfp4_output_error_workspace_size(tokens: int, out: int, inp: int) -> int:
+    return int(_lib.nvfp4_output_error_workspace_size(tokens, out, inp))
+
+
+def nvfp4_output_error(X, tokens, inp, ldx, W, out, ldw, scales, packed, S, err, accumulate,
+                       workspace, stream=None, prepare=False):
+    _need(err, out, "err")
+    return _run("nvfp4_output_error", (
+        _dev(X, "X", (torch.bfloat16,)), DTYPE_BF16, tokens, inp, ldx,
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), out, ldw,
+        _dev(scales, "scales", (torch.uint8,)), _dev(packed, "packed", (torch.uint8,)),
+        _dev(S, "S", (torch.float32,)), _dev(err, "err", (torch.float64,)), int(accumulate),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), prepare)
+
+
 # --- convenience wrappers (allocate outputs with torch, then call the entry points) ----------
 
 def _bmat(W: torch.Tensor):
@@ -302,6 +321,23 @@ def scale_search_proposal(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tens
                                 stride_h, objective, lo, hi, center, incoming, S, scales, packed,
                                 loss, offset, stream)
     return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def output_error(X: torch.Tensor, W: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+                 S: torch.Tensor, err: torch.Tensor | None = None, accumulate: bool = False,
+                 stream=None) -> torch.Tensor:
+    """Per-row layer-output error err[o] = sum_t (X (W - W_hat)^T)[t, o]^2 (float64 [out])."""
+    T, n = X.shape
+    o = W.shape[0]
+    if X.stride(1) != 1 or W.stride(1) != 1:
+        raise ValueError("X and W rows must be contiguous")
+    if err is None:
+        err = torch.empty(o, dtype=torch.float64, device=X.device)
+    ws = torch.empty(max(16, nvfp4_output_error_workspace_size(T, o, n)), dtype=torch.uint8,
+                     device=X.device)
+    nvfp4_output_error(X, T, n, X.stride(0), W, o, W.stride(0), scales.contiguous(),
+                       packed.contiguous(), S, err, accumulate, ws, stream)
+    return err
 
 
 def pack(W: torch.Tensor, scales: torch.Tensor, S: torch.Tensor, stream=None) -> torch.Tensor:

@@ -194,6 +194,39 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
                         int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
                         uint8_t* packed, void* stream);
 
+/* ---------------------------------------------------------------------------------------------
+ * Evaluation: layer-output error of a quantised layer ([HS] §3: the layer-output reconstruction
+ * criterion; the activation-loss comparison of Min-Max, MSE-guided and Hessian-guided scales).
+ *
+ *   w_hat[o, i] = sign * fl(level * eff[c]) from packed[o, i/2] (element 2k in the low nibble)
+ *                 and scales[o, i/16], eff[c] = fl(S[0] * E4M3(c)); scale byte 0 gives zeros
+ *   err[o]      = sum_t (sum_i x[t, i] * (w[o, i] - w_hat[o, i]))^2   (+ err[o] if accumulate)
+ *
+ * Computed on MFMA: E = fl(w - w_hat) in binary32 is split into two bf16 matrices E_hi + E_lo
+ * (16 significant bits of E), Y = X E_hi^T + X E_lo^T is accumulated in binary32, and the
+ * squares of Y are summed per row, over each 128-token tile in binary32 and over tiles in
+ * binary64. Deterministic. Relative to the exact binary64 value, err[o] agrees to about 1e-5
+ * for activations and residuals without extreme cancellation (the tests use 1e-4).
+ *
+ * X         device, bf16 [tokens, in], row stride ldx (multiple of 8), 16-byte aligned.
+ * W         device, bf16 or f32 [out, in], row stride ldw (16-byte aligned rows), the weights
+ *           that were quantised.
+ * scales    device, uint8 [out, in/16], codes 0..126; packed device, uint8 [out, in/2],
+ *           4-byte aligned; S device float [1] (the global scale the codes were made with).
+ * err       device, double [out], 8-byte aligned; written, or added to when accumulate != 0
+ *           (token chunks of one calibration set).
+ * workspace device, at least nvfp4_output_error_workspace_size(tokens, out, in) bytes,
+ *           16-byte aligned, no initialisation needed (holds E_hi, E_lo and the tile partials).
+ * Requires in % 16 == 0 and tokens <= 65535 * 128. tokens == 0 or in == 0 only writes err.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in);
+
+nvfp4_status nvfp4_output_error(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                int64_t ldx, const void* W, int w_dtype, int64_t out, int64_t ldw,
+                                const uint8_t* scales, const uint8_t* packed, const float* S,
+                                double* err, int accumulate, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

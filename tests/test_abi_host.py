@@ -23,7 +23,7 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("nvfp4_diag_hessian", "nvfp4_diag_hessian_batched", "nvfp4_global_scale",
                  "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
-                 "nvfp4_status_string",
+                 "nvfp4_output_error", "nvfp4_output_error_workspace_size", "nvfp4_status_string",
                  "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
         assert want in names
 
@@ -111,6 +111,33 @@ def test_scale_search_proposal_rejects_bad_arguments(lib):
     assert _proposal(lib, dt=3) == n.ERR_DTYPE
     assert _proposal(lib, inp=40, ldw=40) == n.ERR_SHAPE
     assert _proposal(lib, out=0, cen=None) == n.OK                # empty: nothing enqueued
+
+
+def test_output_error_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    oe = lib.nvfp4_output_error
+    need = lib.nvfp4_output_error_workspace_size(256, 4, 64)
+    assert need > 0
+    ok = dict(X=FAKE, xd=1, T=256, inp=64, ldx=64, W=FAKE, wd=1, out=4, ldw=64, sc=FAKE, pk=FAKE,
+              S=FAKE, err=FAKE, acc=0, ws=FAKE, wsb=need)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return oe(a["X"], a["xd"], a["T"], a["inp"], a["ldx"], a["W"], a["wd"], a["out"], a["ldw"],
+                  a["sc"], a["pk"], a["S"], a["err"], a["acc"], a["ws"], a["wsb"], None)
+    assert call(xd=0) == n.ERR_DTYPE                              # X must be bf16
+    assert call(wd=4) == n.ERR_DTYPE
+    assert call(inp=40, ldx=40, ldw=40) == n.ERR_SHAPE
+    assert call(ldx=60) == n.ERR_SHAPE                            # ldx < in
+    assert call(T=-1) == n.ERR_SHAPE
+    assert call(T=65536 * 128) == n.ERR_SHAPE
+    assert call(err=None) == n.ERR_NULL
+    assert call(pk=None) == n.ERR_NULL
+    assert call(X=ODD) == n.ERR_ALIGN
+    assert call(ws=None) == n.ERR_WORKSPACE
+    assert call(wsb=need - 1) == n.ERR_WORKSPACE
+    assert call(out=0, err=None) == n.OK
 
 
 def test_pack_and_global_scale_reject_bad_arguments(lib):
