@@ -8,12 +8,14 @@
 //           matrices E_hi = bf16(E) and E_lo = bf16(E - E_hi) (round to nearest even; E - E_hi is
 //           exact), so E_hi + E_lo carries 16 significant bits of E.
 //   gemm:   Y = X E_hi^T + X E_lo^T on MFMA (v_mfma_f32_32x32x16_bf16, binary32 accumulation).
-//           A workgroup of 4 waves owns a 128-token x 128-row tile; each wave a 64 x 64 quarter
-//           as 2 x 2 MFMA tiles of 32 x 32. K advances by 32: X and both E tiles are staged
-//           through LDS (double-buffered, rows padded to 80 B), the next stage's global loads in
-//           flight during the current stage's MFMAs. The epilogue squares Y and sums each
-//           column over the tile's 128 tokens (fixed order), writing one binary32 partial per
-//           (token tile, row).
+//           A workgroup of 4 waves owns a 256-token x 128-row tile; each wave a 128 x 64 part
+//           as 4 x 2 MFMA tiles of 32 x 32 (16 MFMAs per 8 LDS fragment reads). K advances by
+//           32: X and both E tiles are staged through LDS (64 KB, double-buffered, 16-byte
+//           chunks XOR-swizzled per row against bank conflicts), the next stage's global loads
+//           in flight during the current stage's MFMAs. At 223 VGPRs two workgroups share a CU
+//           (two waves per SIMD). Tiles are dealt to the XCDs in groups of 4 x 8 that share K
+//           slices in L2. The epilogue squares Y and sums each column over the tile's 256
+//           tokens (fixed order), writing one binary32 partial per (token tile, row).
 //   reduce: one thread per row adds the token-tile partials in order in binary64 (and the
 //           running err when accumulating over token chunks).
 // No atomics: the result is deterministic.
@@ -97,61 +99,101 @@ __global__ __launch_bounds__(256) void k_residual_split(
 
 // ---- gemm + squared-sum epilogue ------------------------------------------------------------
 
-constexpr int BM = 128;      // tokens per tile
+constexpr int BM = 256;      // tokens per tile
 constexpr int BN = 128;      // output rows per tile
-constexpr int BK = 32;       // reduction step
-constexpr int LDK = BK + 8;  // padded LDS row (bf16 elements): 80 B
+constexpr int BK = 32;       // reduction step: an LDS row is 64 B = 4 chunks of 16 B
+constexpr int kXcds = 8;
 
 struct Stage {
-    uint16_t a[BM][LDK];
-    uint16_t bh[BN][LDK];
-    uint16_t bl[BN][LDK];
+    uint16_t a[BM][BK];
+    uint16_t bh[BN][BK];
+    uint16_t bl[BN][BK];
 };
+constexpr size_t kGemmLds = 2 * sizeof(Stage);  // 64 KB of dynamic LDS (no opt-in needed)
+static_assert(kGemmLds <= 65536, "dynamic LDS above 64 KB needs hipFuncSetAttribute");
 
-__global__ __launch_bounds__(256) void k_output_gemm(
+// 16-byte chunk c of LDS row r sits at chunk position c ^ swz(r). With this XOR pattern the
+// stores (4 lanes per row, consecutive rows) and the MFMA fragment reads (one chunk of 16 or 32
+// consecutive rows) touch distinct banks in every group of 8 or 16 lanes, for 32 or 64 banks.
+__device__ __forceinline__ int swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+
+// Workgroup -> (token tile, row tile). Workgroups are dealt to the 8 XCDs round-robin; when the
+// tile count is a multiple of 8, XCD x gets the contiguous tile range [x n/8, (x+1) n/8). Within
+// it, tiles come in groups of kGM token tiles x kGN row tiles (32 workgroups, one per CU of the
+// XCD) when the tile grid divides evenly, so the workgroups resident on an XCD at one time read
+// 4 X tiles and 8 E tiles and advance through K together: each K slice comes into the XCD's L2
+// once and is reused there. Otherwise tiles are numbered token-tile-major.
+constexpr uint32_t kGM = 4, kGN = 8;
+
+__device__ __forceinline__ void tile_of(uint32_t L, uint32_t ntn, uint32_t ntm, uint32_t nb,
+                                        uint32_t& tm, uint32_t& tn) {
+    const uint32_t q = (nb % kXcds == 0) ? (L % kXcds) * (nb / kXcds) + L / kXcds : L;
+    if (ntn % kGN == 0 && ntm % kGM == 0) {
+        const uint32_t g = q / (kGM * kGN), l = q % (kGM * kGN);
+        const uint32_t gpr = ntn / kGN;
+        tm = (g / gpr) * kGM + l / kGN;
+        tn = (g % gpr) * kGN + l % kGN;
+    } else {
+        tm = q / ntn;
+        tn = q - tm * ntn;
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_output_gemm(
     const uint16_t* __restrict__ X, int64_t T, int64_t in, int64_t ldx,
     const uint16_t* __restrict__ e_hi, const uint16_t* __restrict__ e_lo, int64_t out,
-    float* __restrict__ partial) {
-    __shared__ Stage st[2];
-    __shared__ float red[2][BN];
+    uint32_t ntn, uint32_t ntm, uint32_t nb, float* __restrict__ partial) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    Stage* st = reinterpret_cast<Stage*>(smem);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int64_t n0 = (int64_t)blockIdx.x * BN;   // output-row tile
-    const int64_t m0 = (int64_t)blockIdx.y * BM;   // token tile
+    const int wm = wave >> 1, wn = wave & 1;   // wave tile: 128 tokens x 64 rows
+    uint32_t tm, tn;
+    tile_of(blockIdx.x, ntn, ntm, nb, tm, tn);
+    const int64_t n0 = (int64_t)tn * BN;
+    const int64_t m0 = (int64_t)tm * BM;
 
-    // global -> register staging: 512 16-byte chunks per matrix tile, 2 per thread
-    uint4 ra[2], rh[2], rl[2];
+    // global -> register staging of one K step: X 1024 chunks of 16 B (4 per thread), E_hi and
+    // E_lo 512 each (2 per thread)
+    uint4 ra[4], rh[2], rl[2];
     auto load = [&](int64_t k0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int id = tid + 256 * r;
+            const int row = id >> 2, ch = id & 3;
+            const int64_t k = k0 + ch * 8, t = m0 + row;
+            ra[r] = (k < in && t < T) ? *reinterpret_cast<const uint4*>(X + t * ldx + k)
+                                      : make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int id = tid + 256 * r;
             const int row = id >> 2, ch = id & 3;
-            const int64_t k = k0 + ch * 8;
-            const bool kin = k < in;
-            const int64_t t = m0 + row, o = n0 + row;
-            ra[r] = (kin && t < T) ? *reinterpret_cast<const uint4*>(X + t * ldx + k)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-            rh[r] = (kin && o < out) ? *reinterpret_cast<const uint4*>(e_hi + o * in + k)
-                                     : make_uint4(0u, 0u, 0u, 0u);
-            rl[r] = (kin && o < out) ? *reinterpret_cast<const uint4*>(e_lo + o * in + k)
-                                     : make_uint4(0u, 0u, 0u, 0u);
+            const int64_t k = k0 + ch * 8, o = n0 + row;
+            const bool ok = k < in && o < out;
+            rh[r] = ok ? *reinterpret_cast<const uint4*>(e_hi + o * in + k) : make_uint4(0u, 0u, 0u, 0u);
+            rl[r] = ok ? *reinterpret_cast<const uint4*>(e_lo + o * in + k) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     auto store = [&](Stage& s) {
 #pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int id = tid + 256 * r;
+            const int row = id >> 2;
+            *reinterpret_cast<uint4*>(&s.a[row][((id & 3) ^ swz(row)) * 8]) = ra[r];
+        }
+#pragma unroll
         for (int r = 0; r < 2; ++r) {
             const int id = tid + 256 * r;
-            const int row = id >> 2, ch = id & 3;
-            *reinterpret_cast<uint4*>(&s.a[row][ch * 8]) = ra[r];
-            *reinterpret_cast<uint4*>(&s.bh[row][ch * 8]) = rh[r];
-            *reinterpret_cast<uint4*>(&s.bl[row][ch * 8]) = rl[r];
+            const int row = id >> 2, c = ((id & 3) ^ swz(row)) * 8;
+            *reinterpret_cast<uint4*>(&s.bh[row][c]) = rh[r];
+            *reinterpret_cast<uint4*>(&s.bl[row][c]) = rl[r];
         }
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[4][2];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
@@ -167,15 +209,21 @@ __global__ __launch_bounds__(256) void k_output_gemm(
         if (it + 1 < nk) load((it + 1) * BK);
 #pragma unroll
         for (int kk = 0; kk < BK; kk += 16) {
-            bf16x8 fa[2], fh[2], fl[2];
+            const int c = (kk + kg) >> 3;          // logical chunk of this lane's 8 K values
+            bf16x8 fa[4], fh[2], fl[2];
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                fa[t] = *reinterpret_cast<const bf16x8*>(&st[cur].a[wm * 64 + t * 32 + r32][kk + kg]);
-                fh[t] = *reinterpret_cast<const bf16x8*>(&st[cur].bh[wn * 64 + t * 32 + r32][kk + kg]);
-                fl[t] = *reinterpret_cast<const bf16x8*>(&st[cur].bl[wn * 64 + t * 32 + r32][kk + kg]);
+            for (int t = 0; t < 4; ++t) {
+                const int row = wm * 128 + t * 32 + r32;
+                fa[t] = *reinterpret_cast<const bf16x8*>(&st[cur].a[row][(c ^ swz(row)) * 8]);
             }
 #pragma unroll
-            for (int a = 0; a < 2; ++a)
+            for (int t = 0; t < 2; ++t) {
+                const int row = wn * 64 + t * 32 + r32;
+                fh[t] = *reinterpret_cast<const bf16x8*>(&st[cur].bh[row][(c ^ swz(row)) * 8]);
+                fl[t] = *reinterpret_cast<const bf16x8*>(&st[cur].bl[row][(c ^ swz(row)) * 8]);
+            }
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
 #pragma unroll
                 for (int b = 0; b < 2; ++b) {
                     acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a], fh[b], acc[a][b], 0, 0, 0);
@@ -186,34 +234,44 @@ __global__ __launch_bounds__(256) void k_output_gemm(
         __syncthreads();
     }
 
-    // epilogue: lane holds rows i = (e/4)*8 + (lane/32)*4 + e%4 of column j = lane%32 of each
-    // 32x32 tile; sum the squares over the lane's rows and tiles, then over the lane pair.
+    // epilogue: a lane holds rows i = (e/4)*8 + (lane/32)*4 + e%4 of column j = lane%32 of each
+    // 32x32 tile; sum the squares over the lane's rows and row tiles, then over the lane pair,
+    // then over the two waves of the same columns (stage memory is free after the last sync)
+    float* red = reinterpret_cast<float*>(smem);  // [2][BN]
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
         float s = 0.0f;
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < 4; ++a)
 #pragma unroll
             for (int e = 0; e < 16; ++e) s = __builtin_fmaf(acc[a][b][e], acc[a][b][e], s);
         s += __shfl_xor(s, 32, 64);
-        if (lane < 32) red[wm][wn * 64 + b * 32 + lane] = s;
+        if (lane < 32) red[wm * BN + wn * 64 + b * 32 + lane] = s;
     }
     __syncthreads();
     if (tid < BN) {
         const int64_t o = n0 + tid;
-        if (o < out) partial[(int64_t)blockIdx.y * out + o] = red[0][tid] + red[1][tid];
+        if (o < out) partial[(int64_t)tm * out + o] = red[tid] + red[BN + tid];
     }
 }
 
 // ---- reduce -------------------------------------------------------------------------------
 
+// One thread per row; the token-tile partials are added in order, 8 loads in flight.
 __global__ __launch_bounds__(256) void k_output_reduce(const float* __restrict__ partial,
                                                        int64_t tiles, int64_t out,
                                                        double* __restrict__ err, int accumulate) {
     const int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (o >= out) return;
     double s = accumulate ? err[o] : 0.0;
-    for (int64_t t = 0; t < tiles; ++t) s += (double)partial[t * out + o];
+    for (int64_t t0 = 0; t0 < tiles; t0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = (t0 + k < tiles) ? partial[(t0 + k) * out + o] : 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (t0 + k < tiles) s += (double)v[k];
+    }
     err[o] = s;
 }
 
@@ -249,10 +307,11 @@ hipError_t launch_output_error(const void* X, int64_t tokens, int64_t in, int64_
                                e_hi, e_lo);
     }
     if (tiles > 0) {
-        const dim3 ggrid((uint32_t)((out + BN - 1) / BN), (uint32_t)tiles);
-        hipLaunchKernelGGL(k_output_gemm, ggrid, dim3(256), 0, stream,
-                           static_cast<const uint16_t*>(X), tokens, in, ldx, e_hi, e_lo, out,
-                           partial);
+        const uint32_t ntn = (uint32_t)((out + BN - 1) / BN);
+        const uint32_t nb = ntn * (uint32_t)tiles;
+        hipLaunchKernelGGL(k_output_gemm, dim3(nb), dim3(256), kGemmLds, stream,
+                           static_cast<const uint16_t*>(X), tokens, in, ldx, e_hi, e_lo, out, ntn,
+                           (uint32_t)tiles, nb, partial);
     }
     hipLaunchKernelGGL(k_output_reduce, dim3((uint32_t)((out + 255) / 256)), dim3(256), 0, stream,
                        partial, tiles, out, err, accumulate ? 1 : 0);

@@ -204,7 +204,7 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
  *
  * Computed on MFMA: E = fl(w - w_hat) in binary32 is split into two bf16 matrices E_hi + E_lo
  * (16 significant bits of E), Y = X E_hi^T + X E_lo^T is accumulated in binary32, and the
- * squares of Y are summed per row, over each 128-token tile in binary32 and over tiles in
+ * squares of Y are summed per row, over each 256-token tile in binary32 and over tiles in
  * binary64. Deterministic. Relative to the exact binary64 value, err[o] agrees to about 1e-5
  * for activations and residuals without extreme cancellation (the tests use 1e-4).
  *
@@ -217,7 +217,8 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
  *           (token chunks of one calibration set).
  * workspace device, at least nvfp4_output_error_workspace_size(tokens, out, in) bytes,
  *           16-byte aligned, no initialisation needed (holds E_hi, E_lo and the tile partials).
- * Requires in % 16 == 0 and tokens <= 65535 * 128. tokens == 0 or in == 0 only writes err.
+ * Requires in % 16 == 0 and ceil(out/128) * ceil(tokens/256) < 2^31. tokens == 0 or in == 0
+ * only writes err.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in);
 

@@ -131,7 +131,7 @@ def test_output_error_rejects_bad_arguments(lib):
     assert call(inp=40, ldx=40, ldw=40) == n.ERR_SHAPE
     assert call(ldx=60) == n.ERR_SHAPE                            # ldx < in
     assert call(T=-1) == n.ERR_SHAPE
-    assert call(T=65536 * 128) == n.ERR_SHAPE
+    assert call(T=1 << 40, out=1 << 20, ldw=64) == n.ERR_SHAPE   # tile count >= 2^31
     assert call(err=None) == n.ERR_NULL
     assert call(pk=None) == n.ERR_NULL
     assert call(X=ODD) == n.ERR_ALIGN
