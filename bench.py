@@ -295,6 +295,9 @@ def main():
                     help="record per-call HIP events on every Nth timed step (1 = all)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="run one 1 GiB device copy (counter calibration for rocprofv3 --pmc)")
+    ap.add_argument("--activations", action="store_true",
+                    help="also time on-line activation quantisation (dynamic S + MSE [-3,7]) of "
+                         "the first token chunk and of a 16-token decode batch, outside the step")
     ap.add_argument("--output-error", action="store_true",
                     help="also time the layer-output error evaluation (MFMA) of the last mode's "
                          "codes over the first token chunk, outside the step")
@@ -424,6 +427,48 @@ def main():
                       "algorithmic flops; the time includes the residual split and the "
                       "reduction kernels"}
 
+    # on-line activation quantisation (outside the step): one kernel pair vs global scale +
+    # search (three kernels), on a prefill chunk and a decode batch
+    acts = None
+    if args.activations:
+        acts = {}
+        X0 = runner.sets[0].chunks[0]
+        for name, Xa in (("prefill", X0), ("tokens1024", X0[:1024]), ("tokens256", X0[:256]),
+                         ("decode16", X0[:16])):
+            Ta, na = Xa.shape
+            Sx = torch.empty(1, dtype=torch.float32, device=dev)
+            sc = torch.empty(Ta * (na // 16), dtype=torch.uint8, device=dev)
+            pk = torch.empty(Ta * (na // 2), dtype=torch.uint8, device=dev)
+            wsa = torch.empty(max(16, nv.nvfp4_quantize_activations_workspace_size(Ta, na)),
+                              dtype=torch.uint8, device=dev)
+            wsg = torch.empty(max(16, nv.nvfp4_global_scale_workspace_size(1, Ta, na)),
+                              dtype=torch.uint8, device=dev)
+            one = nv.nvfp4_quantize_activations(Xa, Ta, na, na, nv.MSE, None, -3, 7,
+                                                nv.GS_AMAX_256, Sx, sc, pk, wsa, prepare=True)
+            gs = nv.nvfp4_global_scale(Xa, 1, Ta, na, na, Ta * na, nv.GS_AMAX_256, Sx, wsg,
+                                       prepare=True)
+            se = nv.nvfp4_scale_search(Xa, 1, Ta, na, na, Ta * na, 16, None, 0, nv.MSE, -3, 7,
+                                       False, Sx, sc, pk, prepare=True)
+
+            def timed(fn, reps=200):
+                for _ in range(5):
+                    fn()
+                torch.cuda.synchronize()
+                p0.record(main)
+                for _ in range(reps):
+                    fn()
+                p1.record(main)
+                torch.cuda.synchronize()
+                return p0.elapsed_time(p1) * 1e3 / reps
+
+            us1 = timed(one)
+            us2 = timed(lambda: (gs(), se()))
+            nbytes = Ta * na * 2 + Ta * na // 2 + Ta * na // 16
+            acts[name] = {"tokens": Ta, "in": na, "us": round(us1, 2),
+                          "us_global_scale_then_search": round(us2, 2),
+                          "GB/s": round(nbytes / us1 / 1e3, 1),
+                          "weights/s": Ta * na / (us1 * 1e-6)}
+
     per_label = {}
     for row in ev:
         for lab, (e0, e1) in zip(labels, row):
@@ -503,6 +548,8 @@ def main():
     }
     if oe is not None:
         line["output_error"] = oe
+    if acts is not None:
+        line["activations"] = acts
     print(json.dumps(line), flush=True)
 
 

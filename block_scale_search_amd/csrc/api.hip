@@ -11,6 +11,12 @@ namespace {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
+nvfp4::ScaleSource given_scale(const float* S) {
+    nvfp4::ScaleSource src;
+    src.S = S;
+    return src;
+}
+
 int elem_size(int dtype) {
     if (dtype == NVFP4_DTYPE_F32) return 4;
     if (dtype == NVFP4_DTYPE_BF16) return 2;
@@ -156,8 +162,8 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
         return NVFP4_ERR_ALIGN;
     return hip_status(nvfp4::launch_scale_search(
         W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw, stride_w, wmse ? h : nullptr,
-        wmse ? stride_h : 0, wmse, lo, hi, exhaustive != 0, S, scales, packed, loss, offset,
-        nullptr, nullptr, static_cast<hipStream_t>(stream)));
+        wmse ? stride_h : 0, wmse, lo, hi, exhaustive != 0, given_scale(S), scales, packed, loss,
+        offset, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_scale_search_proposal(const void* W, int w_dtype, int64_t batch, int64_t out,
@@ -185,8 +191,8 @@ nvfp4_status nvfp4_scale_search_proposal(const void* W, int w_dtype, int64_t bat
         return NVFP4_ERR_ALIGN;
     return hip_status(nvfp4::launch_scale_search(
         W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw, stride_w, wmse ? h : nullptr,
-        wmse ? stride_h : 0, wmse, lo, hi, false, S, scales, packed, loss, offset, center,
-        incoming, static_cast<hipStream_t>(stream)));
+        wmse ? stride_h : 0, wmse, lo, hi, false, given_scale(S), scales, packed, loss, offset,
+        center, incoming, static_cast<hipStream_t>(stream)));
 }
 
 nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, int64_t in,
@@ -200,6 +206,63 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
     return hip_status(nvfp4::launch_pack(W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw,
                                          stride_w, scales, S, packed,
                                          static_cast<hipStream_t>(stream)));
+}
+
+// On-line activation quantisation: up to kFusedElems elements the search kernel reduces the
+// amax partials itself (two kernels); above, the per-workgroup reduction of the partials costs
+// more than the launch it saves (measured on MI355X), so the global scale runs as its own two
+// kernels and the search reads S. Both give the same bits.
+constexpr int64_t kFusedElems = (int64_t)1 << 23;
+
+size_t nvfp4_quantize_activations_workspace_size(int64_t tokens, int64_t in) {
+    if (tokens < 0 || in < 0) return 0;
+    // [S slot, 256 B][amax partials]
+    return 256 + (size_t)nvfp4::amax_partial_count(1, tokens, in) * sizeof(uint32_t);
+}
+
+nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                        int64_t ldx, int objective, const float* h, int32_t lo,
+                                        int32_t hi, int rule, float* S_out, uint8_t* scales,
+                                        uint8_t* packed, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
+    if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
+    if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return NVFP4_ERR_WINDOW;
+    nvfp4_status st = check_weights(X, x_dtype, 1, tokens, in, ldx, tokens * ldx);
+    if (st != NVFP4_OK) return st;
+    if (tokens == 0 || in == 0) return NVFP4_OK;
+    const bool wmse = objective == NVFP4_WMSE;
+    if (scales == nullptr || packed == nullptr || (wmse && h == nullptr)) return NVFP4_ERR_NULL;
+    if (!aligned8(packed) || (S_out && (reinterpret_cast<uintptr_t>(S_out) & 3u)) ||
+        (wmse && !aligned16(h)))
+        return NVFP4_ERR_ALIGN;
+    const size_t need = nvfp4_quantize_activations_workspace_size(tokens, in);
+    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    const bool bf16 = x_dtype == NVFP4_DTYPE_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    float* S_slot = static_cast<float*>(workspace);
+    uint32_t* partial = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(workspace) + 256);
+    nvfp4::ScaleSource src;
+    if (tokens * in <= kFusedElems) {
+        hipError_t e = nvfp4::launch_amax_partial(X, bf16, 1, tokens, in, ldx, tokens * ldx,
+                                                  partial, s);
+        if (e != hipSuccess) return hip_status(e);
+        src.amax_partial = partial;
+        src.n_partial = nvfp4::amax_partial_count(1, tokens, in);
+        src.rule = rule;
+        src.S_out = S_out;
+    } else {
+        float* S = S_out ? S_out : S_slot;
+        hipError_t e = nvfp4::launch_global_scale(X, bf16, 1, tokens, in, ldx, tokens * ldx, rule,
+                                                  S, partial, s);
+        if (e != hipSuccess) return hip_status(e);
+        src.S = S;
+    }
+    return hip_status(nvfp4::launch_scale_search(X, bf16, 1, tokens, in, ldx, tokens * ldx,
+                                                 wmse ? h : nullptr, 0, wmse, lo, hi, false, src,
+                                                 scales, packed, nullptr, nullptr, nullptr,
+                                                 nullptr, s));
 }
 
 size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in) {

@@ -115,11 +115,14 @@ size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in) {
     return (size_t)batch * (size_t)amax_blocks(batch, out, in) * sizeof(uint32_t);
 }
 
-hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
-                               int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
+int64_t amax_partial_count(int64_t batch, int64_t out, int64_t in) {
+    return amax_blocks(batch, out, in);
+}
+
+hipError_t launch_amax_partial(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, uint32_t* partial,
                                hipStream_t stream) {
     const int64_t nblk = amax_blocks(batch, out, in);
-    uint32_t* partial = static_cast<uint32_t*>(workspace);
     const int esz = bf16 ? 2 : 4;
     const int64_t vpr = in / (bf16 ? 8 : 4);
     // chunk: whole 4 KB wave-rows of vectors, so every workgroup starts on a 4 KB boundary of a
@@ -135,6 +138,16 @@ hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t 
         hipLaunchKernelGGL(k_amax_partial<false>, grid, dim3(kThreads), 0, stream,
                            static_cast<const uint8_t*>(W), out, vpr, ldw * esz, stride_w * esz,
                            chunk, partial);
+    return hipGetLastError();
+}
+
+hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
+                               hipStream_t stream) {
+    const int64_t nblk = amax_blocks(batch, out, in);
+    uint32_t* partial = static_cast<uint32_t*>(workspace);
+    const hipError_t e = launch_amax_partial(W, bf16, batch, out, in, ldw, stride_w, partial, stream);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_global_scale_finalize, dim3((uint32_t)batch), dim3(kThreads), 0, stream,
                        partial, nblk, rule, S);
     return hipGetLastError();

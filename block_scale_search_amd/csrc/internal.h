@@ -29,11 +29,28 @@ hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t 
                                int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,
                                hipStream_t stream);
 
+// Pass 1 of the global scale alone (per-workgroup partial maxima, amax_partial_count of them
+// per matrix), for callers that reduce the partials themselves.
+int64_t amax_partial_count(int64_t batch, int64_t out, int64_t in);
+hipError_t launch_amax_partial(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
+                               int64_t ldw, int64_t stride_w, uint32_t* partial,
+                               hipStream_t stream);
+
+// Where the search takes S from: S[batch] as given, or (one matrix) reduced in every
+// workgroup from the amax partials with the rule, workgroup 0 also writing it to S_out.
+struct ScaleSource {
+    const float* S = nullptr;
+    const uint32_t* amax_partial = nullptr;
+    int64_t n_partial = 0;
+    int rule = 0;
+    float* S_out = nullptr;
+};
+
 // center == NULL: plain window (around the base code) or exhaustive search. center != NULL:
 // window around center[] with the optional incoming[] code kept on ties (exhaustive false).
 hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
-                               bool wmse, int lo, int hi, bool exhaustive, const float* S,
+                               bool wmse, int lo, int hi, bool exhaustive, ScaleSource src,
                                uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
                                const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream);

@@ -323,20 +323,41 @@ __device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
     return *flag == 0;
 }
 
+// S of one matrix from its amax partials (bit patterns of non-negative binary32 values), by the
+// same formula as the global-scale kernel: amax / 2688 or amax / 1536, 1 for amax = 0.
+__device__ __forceinline__ float scale_from_partials(const uint32_t* __restrict__ partial,
+                                                     int64_t n, int rule, uint32_t* wmax) {
+    uint32_t m = 0u;
+    for (int64_t i = threadIdx.x; i < n; i += kSearchThreads) m = max(m, partial[i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    uint32_t r = wmax[0];
+#pragma unroll
+    for (int i = 1; i < kSearchThreads / 64; ++i) r = max(r, wmax[i]);
+    const float amax = __uint_as_float(r);
+    return amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
+}
+
 // PROPOSAL: the window is centred on a per-group proposal code center[] instead of the base
 // code, and a valid incoming code incoming[] (if given) is scored as well and kept on ties.
-template <bool BF16, bool WMSE, int NWIN, bool PROPOSAL>
+// SFP: S is reduced from amax partials in every workgroup (one matrix; workgroup 0 stores it)
+// instead of read from S[].
+template <bool BF16, bool WMSE, int NWIN, bool PROPOSAL, bool SFP>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
     uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h,
-    int lo, int hi, int exhaustive, const float* __restrict__ S_arr, uint8_t* __restrict__ scales,
+    int lo, int hi, int exhaustive, ScaleSource src, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out,
     const uint8_t* __restrict__ center, const uint8_t* __restrict__ incoming) {
     __shared__ float2 tab[128];
     __shared__ int flag;
+    __shared__ uint32_t wmax[kSearchThreads / 64];
     const int64_t batch = blockIdx.y;
-    const bool octave_ok = build_table(S_arr[batch], tab, &flag);
 
+    // the group's weights and h are loaded first: S and the code table, which need a
+    // workgroup-wide step, are computed while these loads are in flight
     const uint32_t gpr = in >> 4;
     const uint32_t G = out * gpr;
     const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
@@ -367,13 +388,22 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
         }
     }
 
+    float S;
+    if constexpr (SFP) {
+        S = scale_from_partials(src.amax_partial, src.n_partial, src.rule, wmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0 && src.S_out) src.S_out[0] = S;
+    } else {
+        S = src.S[batch];
+    }
+    const bool octave_ok = build_table(S, tab, &flag);
+
     // Base code: E4M3 round-to-nearest-even of (absmax / 6) / S, at least 1; 0 = zero group.
     float amax = 0.0f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(w[j]));
     int b = 0;
     if (amax > 0.0f) {
-        const float s_star = __fdiv_rn(__fdiv_rn(amax, 6.0f), S_arr[batch]);
+        const float s_star = __fdiv_rn(__fdiv_rn(amax, 6.0f), S);
         b = max(e4m3_rne_sat(s_star), 1);
     }
     const bool live = valid && b > 0;
@@ -433,48 +463,93 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
 
 }  // namespace
 
+namespace {
+
+struct SearchArgs {
+    const uint8_t* W;
+    uint32_t out, in;
+    uint64_t magic;
+    uint32_t shift;
+    int64_t ldw_bytes, stride_w_bytes;
+    const float* h;
+    int64_t stride_h;
+    int lo, hi, exhaustive;
+    ScaleSource src;
+    uint8_t *scales, *packed;
+    float* loss;
+    int8_t* offset;
+    const uint8_t *center, *incoming;
+};
+
+template <bool B, bool M, int N, bool P, bool SFP>
+void launch_one(const SearchArgs& a, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((k_scale_search<B, M, N, P, SFP>), grid, dim3(kSearchThreads), 0, stream,
+                       a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes, a.stride_w_bytes, a.h,
+                       a.stride_h, a.lo, a.hi, a.exhaustive, a.src, a.scales, a.packed, a.loss,
+                       a.offset, a.center, a.incoming);
+}
+
+// window length at compile time where it is one of the pages' windows (16 and 11 codes) or a
+// half-window of 4 around a proposal (9 codes); 0 = run-time length or exhaustive
+template <bool B, bool M>
+void launch_modes(const SearchArgs& a, int nwin, bool proposal, bool sfp, dim3 grid,
+                  hipStream_t stream) {
+    if (proposal) {
+        if (nwin == 9) launch_one<B, M, 9, true, false>(a, grid, stream);
+        else launch_one<B, M, 0, true, false>(a, grid, stream);
+    } else if (sfp) {
+        if (nwin == 16) launch_one<B, M, 16, false, true>(a, grid, stream);
+        else if (nwin == 11) launch_one<B, M, 11, false, true>(a, grid, stream);
+        else launch_one<B, M, 0, false, true>(a, grid, stream);
+    } else {
+        if (nwin == 16) launch_one<B, M, 16, false, false>(a, grid, stream);
+        else if (nwin == 11) launch_one<B, M, 11, false, false>(a, grid, stream);
+        else launch_one<B, M, 0, false, false>(a, grid, stream);
+    }
+}
+
+}  // namespace
+
 hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, const float* h, int64_t stride_h,
-                               bool wmse, int lo, int hi, bool exhaustive, const float* S,
+                               bool wmse, int lo, int hi, bool exhaustive, ScaleSource src,
                                uint8_t* scales, uint8_t* packed, float* loss, int8_t* offset,
                                const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream) {
     const int64_t gpr = in / 16;
     const int64_t G = out * gpr;
-    uint64_t magic;
-    uint32_t shift;
-    gpr_divisor(gpr, magic, shift);
-    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
+    SearchArgs a;
+    gpr_divisor(gpr, a.magic, a.shift);
     const int esz = bf16 ? 2 : 4;
-    const uint8_t* Wb = static_cast<const uint8_t*>(W);
+    a.W = static_cast<const uint8_t*>(W);
+    a.out = (uint32_t)out;
+    a.in = (uint32_t)in;
+    a.ldw_bytes = ldw * esz;
+    a.stride_w_bytes = stride_w * esz;
+    a.h = h;
+    a.stride_h = stride_h;
+    a.lo = lo;
+    a.hi = hi;
+    a.exhaustive = exhaustive ? 1 : 0;
+    a.src = src;
+    a.scales = scales;
+    a.packed = packed;
+    a.loss = loss;
+    a.offset = offset;
+    a.center = center;
+    a.incoming = incoming;
+    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
     const int n = hi - lo + 1;
     const bool proposal = center != nullptr;
-    // windows with a compile-time length: 16 and 11 (the pages' windows), 9 (a half-window of 4
-    // around a proposal)
+    const bool sfp = src.amax_partial != nullptr;
     const int nwin = exhaustive ? 0 : (n == 16 || n == 11 || n == 9 ? n : 0);
-#define NVFP4_LAUNCH_SEARCH(B, M, N, P)                                                           \
-    hipLaunchKernelGGL((k_scale_search<B, M, N, P>), grid, dim3(kSearchThreads), 0, stream, Wb,   \
-                       (uint32_t)out, (uint32_t)in, magic, shift, ldw * esz, stride_w * esz, h,   \
-                       stride_h, lo, hi, exhaustive ? 1 : 0, S, scales, packed, loss, offset,     \
-                       center, incoming)
-#define NVFP4_LAUNCH_SEARCH_N(B, M)                                                               \
-    do {                                                                                          \
-        if (proposal) {                                                                           \
-            if (nwin == 9) NVFP4_LAUNCH_SEARCH(B, M, 9, true);                                    \
-            else NVFP4_LAUNCH_SEARCH(B, M, 0, true);                                              \
-        } else if (nwin == 16) NVFP4_LAUNCH_SEARCH(B, M, 16, false);                              \
-        else if (nwin == 11) NVFP4_LAUNCH_SEARCH(B, M, 11, false);                                \
-        else NVFP4_LAUNCH_SEARCH(B, M, 0, false);                                                 \
-    } while (0)
     if (bf16) {
-        if (wmse) NVFP4_LAUNCH_SEARCH_N(true, true);
-        else NVFP4_LAUNCH_SEARCH_N(true, false);
+        if (wmse) launch_modes<true, true>(a, nwin, proposal, sfp, grid, stream);
+        else launch_modes<true, false>(a, nwin, proposal, sfp, grid, stream);
     } else {
-        if (wmse) NVFP4_LAUNCH_SEARCH_N(false, true);
-        else NVFP4_LAUNCH_SEARCH_N(false, false);
+        if (wmse) launch_modes<false, true>(a, nwin, proposal, sfp, grid, stream);
+        else launch_modes<false, false>(a, nwin, proposal, sfp, grid, stream);
     }
-#undef NVFP4_LAUNCH_SEARCH_N
-#undef NVFP4_LAUNCH_SEARCH
     return hipGetLastError();
 }
 

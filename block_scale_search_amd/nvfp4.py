@@ -42,6 +42,9 @@ _SIGS = {
     "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
                                      _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
+    "nvfp4_quantize_activations_workspace_size": ([_I64, _I64], _SZ),
+    "nvfp4_quantize_activations": ([_P, _I, _I64, _I64, _I64, _I, _P, _I32, _I32, _I, _P, _P, _P,
+                                    _P, _SZ, _P], _I),
     "nvfp4_output_error_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_output_error": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _I64, _P, _P, _P, _P, _I,
                             _P, _SZ, _P], _I),
@@ -206,6 +209,23 @@ def nvfp4_pack(W, batch, out, inp, ldw, stride_w, scales, S, packed, stream=None
         _dev(packed, "packed", (torch.uint8,)), _stream(stream)), prepare)
 
 
+def nvfp4_quantize_activations_workspace_size(tokens: int, inp: int) -> int:
+    return int(_lib.nvfp4_quantize_activations_workspace_size(tokens, inp))
+
+
+def nvfp4_quantize_activations(X, tokens, inp, ldx, objective, h, lo, hi, rule, S_out, scales,
+                               packed, workspace, stream=None, prepare=False):
+    G = tokens * (inp // 16)
+    _need(scales, G, "scales")
+    _need(packed, G * 8, "packed")
+    return _run("nvfp4_quantize_activations", (
+        _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx, objective,
+        _dev(h, "h", (torch.float32,)), lo, hi, rule, _dev(S_out, "S_out", (torch.float32,)),
+        _dev(scales, "scales", (torch.uint8,)), _dev(packed, "packed", (torch.uint8,)),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), prepare)
+
+
 def nvfp4_output_error_workspace_size(tokens: int, out: int, inp: int) -> int:
     return int(_lib.nvfp4_output_error_workspace_size(tokens, out, inp))
 
@@ -321,6 +341,23 @@ def scale_search_proposal(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tens
                                 stride_h, objective, lo, hi, center, incoming, S, scales, packed,
                                 loss, offset, stream)
     return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def quantize_activations(X: torch.Tensor, objective: int = MSE, lo: int = -3, hi: int = 7,
+                         rule: int = GS_AMAX_256, h: torch.Tensor | None = None, stream=None):
+    """Dynamic per-tensor S and the scale search + pack of X [tokens, in] in two kernels."""
+    T, n = X.shape
+    if X.stride(1) != 1:
+        raise ValueError("X rows must be contiguous")
+    dev = X.device
+    S = torch.empty(1, dtype=torch.float32, device=dev)
+    scales = torch.empty((T, n // 16), dtype=torch.uint8, device=dev)
+    packed = torch.empty((T, n // 2), dtype=torch.uint8, device=dev)
+    ws = torch.empty(max(16, nvfp4_quantize_activations_workspace_size(T, n)), dtype=torch.uint8,
+                     device=dev)
+    nvfp4_quantize_activations(X, T, n, X.stride(0), objective, h if objective == WMSE else None,
+                               lo, hi, rule, S, scales, packed, ws, stream)
+    return {"S": S, "scales": scales, "packed": packed}
 
 
 def output_error(X: torch.Tensor, W: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

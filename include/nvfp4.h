@@ -195,6 +195,36 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
                         uint8_t* packed, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * On-line activation quantisation ([SS] Experimental Results: the WA, WAKV and WAKVQ settings
+ * quantise activations, KV cache and query states with the same sweep; [SS] §2: the per-tensor
+ * global scale S = max|x| / (256 * 6)).
+ *
+ * For one activation tensor X [tokens, in]: S = max|x| / 1536 (rule AMAX_256) or / 2688
+ * (AMAX_448), 1 for an all-zero tensor, exactly as nvfp4_global_scale computes it; then the
+ * scale search and pack of nvfp4_scale_search with that S (window lo..hi around the base code;
+ * ScaleSweep's MSE window is [-3, 7]). Outputs are bit-identical to nvfp4_global_scale followed
+ * by nvfp4_scale_search. Up to 2^23 elements (decode and small prefill batches) it runs two
+ * kernels instead of three: the search kernel reduces the amax partials itself, which shortens
+ * the launch chain of an inference step. Larger tensors take the three-kernel path, which is
+ * faster there.
+ *
+ * X         device, bf16 or f32 [tokens, in], row stride ldx, 16-byte aligned rows.
+ * objective NVFP4_MSE, or NVFP4_WMSE with h device float [in] (16-byte aligned).
+ * S_out     device float [1] or NULL: receives S.
+ * scales    device uint8 [tokens, in/16]; packed device uint8 [tokens, in/2], 8-byte aligned.
+ * workspace device, at least nvfp4_quantize_activations_workspace_size(tokens, in) bytes,
+ *           16-byte aligned, no initialisation needed.
+ * Requires in % 16 == 0 and tokens * in/16 < 2^31.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_quantize_activations_workspace_size(int64_t tokens, int64_t in);
+
+nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                        int64_t ldx, int objective, const float* h, int32_t lo,
+                                        int32_t hi, int rule, float* S_out, uint8_t* scales,
+                                        uint8_t* packed, void* workspace, size_t workspace_bytes,
+                                        void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Evaluation: layer-output error of a quantised layer ([HS] §3: the layer-output reconstruction
  * criterion; the activation-loss comparison of Min-Max, MSE-guided and Hessian-guided scales).
  *

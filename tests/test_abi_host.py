@@ -23,7 +23,9 @@ def test_header_declares_the_boundary():
     names = _declared()
     for want in ("nvfp4_diag_hessian", "nvfp4_diag_hessian_batched", "nvfp4_global_scale",
                  "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
-                 "nvfp4_output_error", "nvfp4_output_error_workspace_size", "nvfp4_status_string",
+                 "nvfp4_output_error", "nvfp4_output_error_workspace_size",
+                 "nvfp4_quantize_activations", "nvfp4_quantize_activations_workspace_size",
+                 "nvfp4_status_string",
                  "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
         assert want in names
 
@@ -138,6 +140,30 @@ def test_output_error_rejects_bad_arguments(lib):
     assert call(ws=None) == n.ERR_WORKSPACE
     assert call(wsb=need - 1) == n.ERR_WORKSPACE
     assert call(out=0, err=None) == n.OK
+
+
+def test_quantize_activations_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    need = lib.nvfp4_quantize_activations_workspace_size(32, 64)
+    assert need > 0
+
+    def call(**kw):
+        a = dict(X=FAKE, xd=1, T=32, inp=64, ldx=64, obj=0, h=None, lo=-3, hi=7, rule=1, S=FAKE,
+                 sc=FAKE, pk=FAKE, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.nvfp4_quantize_activations(a["X"], a["xd"], a["T"], a["inp"], a["ldx"],
+                                              a["obj"], a["h"], a["lo"], a["hi"], a["rule"],
+                                              a["S"], a["sc"], a["pk"], a["ws"], a["wsb"], None)
+    assert call(obj=3) == n.ERR_ARG
+    assert call(rule=2) == n.ERR_ARG                              # a given S is not on-line
+    assert call(lo=1) == n.ERR_WINDOW
+    assert call(xd=7) == n.ERR_DTYPE
+    assert call(inp=40, ldx=40) == n.ERR_SHAPE
+    assert call(obj=1) == n.ERR_NULL                              # WMSE needs h
+    assert call(sc=None) == n.ERR_NULL
+    assert call(X=ODD) == n.ERR_ALIGN
+    assert call(wsb=need - 1) == n.ERR_WORKSPACE
+    assert call(T=0, X=None) == n.OK
 
 
 def test_pack_and_global_scale_reject_bad_arguments(lib):
