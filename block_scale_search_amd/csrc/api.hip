@@ -79,10 +79,13 @@ static nvfp4_status diag_hessian_impl(const void* X, int x_dtype, const int64_t*
     if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
     if (segments > 1 && segments >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
     if (in == 0) return NVFP4_OK;
-    if (h_acc == nullptr) return NVFP4_ERR_NULL;
+    // h_acc == h == NULL on one segment: deferred accumulation into the workspace
+    const bool deferred = h_acc == nullptr && h == nullptr && seg_offsets == nullptr;
+    if (h_acc == nullptr && !deferred) return NVFP4_ERR_NULL;
     if (tokens > 0 && X == nullptr) return NVFP4_ERR_NULL;
     if (seg_offsets == nullptr && segments > 1) return NVFP4_ERR_NULL;
-    if ((X && !aligned16(X)) || !aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u)))
+    if ((X && !aligned16(X)) || (h_acc && !aligned8(h_acc)) ||
+        (h && (reinterpret_cast<uintptr_t>(h) & 3u)))
         return NVFP4_ERR_ALIGN;
     if (nvfp4::hessian_launch_blocks(tokens, in, segments, x_dtype == NVFP4_DTYPE_BF16) >=
         ((int64_t)1 << 31))
@@ -90,9 +93,11 @@ static nvfp4_status diag_hessian_impl(const void* X, int x_dtype, const int64_t*
     const size_t need = nvfp4::hessian_workspace_bytes(tokens, in, segments);
     if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
     if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    if (deferred && tokens > 0 && (workspace == nullptr || need == 0)) return NVFP4_ERR_WORKSPACE;
     return hip_status(nvfp4::launch_diag_hessian(
         X, x_dtype == NVFP4_DTYPE_BF16, tokens, in, ldx, segments > 1 ? seg_offsets : nullptr,
-        segments, h_acc, h, accumulate != 0, workspace, static_cast<hipStream_t>(stream)));
+        segments, h_acc, h, accumulate != 0, workspace, static_cast<hipStream_t>(stream),
+        deferred ? nvfp4::HessianPass::kPartial : nvfp4::HessianPass::kBoth));
 }
 
 nvfp4_status nvfp4_diag_hessian(const void* X, int x_dtype, int64_t tokens, int64_t in,
@@ -100,6 +105,24 @@ nvfp4_status nvfp4_diag_hessian(const void* X, int x_dtype, int64_t tokens, int6
                                 void* workspace, size_t workspace_bytes, void* stream) {
     return diag_hessian_impl(X, x_dtype, nullptr, 1, tokens, in, ldx, h_acc, h, accumulate,
                              workspace, workspace_bytes, stream);
+}
+
+nvfp4_status nvfp4_diag_hessian_finalize(int x_dtype, int64_t tokens, int64_t in, double* h_acc,
+                                         float* h, int accumulate, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+    const int esz = elem_size(x_dtype);
+    if (esz == 0) return NVFP4_ERR_DTYPE;
+    if (tokens < 0 || in < 0 || in % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (in == 0) return NVFP4_OK;
+    if (h_acc == nullptr) return NVFP4_ERR_NULL;
+    if (!aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u))) return NVFP4_ERR_ALIGN;
+    const size_t need = nvfp4::hessian_workspace_bytes(tokens, in, 1);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_diag_hessian(
+        nullptr, x_dtype == NVFP4_DTYPE_BF16, tokens, in, in, nullptr, 1, h_acc, h,
+        accumulate != 0, workspace, static_cast<hipStream_t>(stream),
+        nvfp4::HessianPass::kFinalize));
 }
 
 nvfp4_status nvfp4_diag_hessian_batched(const void* X, int x_dtype, const int64_t* seg_offsets,

@@ -14,6 +14,10 @@
 //   finalize: eight threads per (segment, column) add interleaved row-group partials with 8
 //             loads in flight each, combine in a fixed order, add the running sum h_acc and
 //             round once to binary32.
+// Deferred mode (one segment): a sequence of token chunks may run the partial pass only, each
+// adding its row-group sums into the workspace slots, and one finalize at the end. The slots
+// of a row group hold binary64 sums of disjoint token sets, so the final sum over slots is the
+// sum over all chunks.
 // The kernel boundary makes the partials of every XCD visible to the finalize kernel.
 // HBM traffic: X once plus 16 B per column per row group (partial written and read back).
 #include <hip/hip_runtime.h>
@@ -114,11 +118,13 @@ __global__ __launch_bounds__(256) void k_hess_group_prefix(const int64_t* __rest
     }
 }
 
+// add != 0: the partial is added to the slot's previous value (deferred accumulation over
+// token chunks) instead of replacing it.
 template <bool BF16, int V>
 __global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restrict__ X,
                                                          int64_t in, int64_t ldx_bytes,
                                                          GroupMap map, int64_t n_strips,
-                                                         double* __restrict__ partial) {
+                                                         double* __restrict__ partial, int add) {
     constexpr int C = XCols<BF16>::kCols;
     constexpr int SW = XCols<BF16>::kStrip;
     __shared__ double red[V][SW];
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restri
         double s = red[0][t];
 #pragma unroll
         for (int q = 1; q < V; ++q) s += red[q][t];
-        if (c < in) partial[grp * in + c] = s;
+        if (c < in) partial[grp * in + c] = add ? partial[grp * in + c] + s : s;
     }
 }
 
@@ -267,7 +273,8 @@ int64_t hessian_launch_blocks(int64_t tokens, int64_t in, int64_t segments, bool
 
 hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t in, int64_t ldx,
                                const int64_t* seg_offsets, int64_t segments, double* h_acc,
-                               float* h, bool accumulate, void* workspace, hipStream_t stream) {
+                               float* h, bool accumulate, void* workspace, hipStream_t stream,
+                               HessianPass pass) {
     const bool batched = seg_offsets != nullptr;
     const int64_t E = batched ? segments : 1;
     GroupMap map{batched ? seg_offsets : nullptr, nullptr, E, tokens,
@@ -286,21 +293,23 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
     const uint8_t* Xb = static_cast<const uint8_t*>(X);
     // measured on MI355X: 8-wave workgroups stream small X faster, 4-wave ones large X
     const bool wide = tokens * in * (bf16 ? 2 : 4) >= kWideBytes;
-    if (blocks > 0) {
+    const int add = (pass == HessianPass::kPartial && accumulate) ? 1 : 0;
+    if (blocks > 0 && pass != HessianPass::kFinalize) {
         const dim3 grid((uint32_t)blocks);
         if (bf16 && wide)
             hipLaunchKernelGGL((k_hess_partial<true, 4>), grid, dim3(256), 0, stream, Xb, in,
-                               ldx_bytes, map, n_strips, partial);
+                               ldx_bytes, map, n_strips, partial, add);
         else if (bf16)
             hipLaunchKernelGGL((k_hess_partial<true, 8>), grid, dim3(512), 0, stream, Xb, in,
-                               ldx_bytes, map, n_strips, partial);
+                               ldx_bytes, map, n_strips, partial, add);
         else if (wide)
             hipLaunchKernelGGL((k_hess_partial<false, 4>), grid, dim3(256), 0, stream, Xb, in,
-                               ldx_bytes, map, n_strips, partial);
+                               ldx_bytes, map, n_strips, partial, add);
         else
             hipLaunchKernelGGL((k_hess_partial<false, 8>), grid, dim3(512), 0, stream, Xb, in,
-                               ldx_bytes, map, n_strips, partial);
+                               ldx_bytes, map, n_strips, partial, add);
     }
+    if (pass == HessianPass::kPartial) return hipGetLastError();
     const dim3 fgrid((uint32_t)((in + kFinCols - 1) / kFinCols), (uint32_t)E);
     hipLaunchKernelGGL(k_hess_finalize, fgrid, dim3(kFinThreads), 0, stream, partial, in, map,
                        h_acc, h, accumulate ? 1 : 0);

@@ -20,9 +20,15 @@ inline void gpr_divisor(int64_t gpr, uint64_t& magic, uint32_t& shift) {
 size_t hessian_workspace_bytes(int64_t tokens, int64_t in, int64_t segments);
 int64_t hessian_launch_blocks(int64_t tokens, int64_t in, int64_t segments, bool bf16);
 
+// kBoth: partial pass then finalize. kPartial: partial pass only, its sums replacing
+// (accumulate false) or added to (accumulate true) the workspace slots. kFinalize: finalize of
+// the slots only (tokens gives the slot layout of the chunks that filled them).
+enum class HessianPass { kBoth, kPartial, kFinalize };
+
 hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t in, int64_t ldx,
                                const int64_t* seg_offsets, int64_t segments, double* h_acc,
-                               float* h, bool accumulate, void* workspace, hipStream_t stream);
+                               float* h, bool accumulate, void* workspace, hipStream_t stream,
+                               HessianPass pass = HessianPass::kBoth);
 
 size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in);
 hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,

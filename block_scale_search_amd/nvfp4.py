@@ -34,6 +34,7 @@ _SIGS = {
     "nvfp4_version": ([], ctypes.c_char_p),
     "nvfp4_diag_hessian_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_diag_hessian": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
+    "nvfp4_diag_hessian_finalize": ([_I, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_diag_hessian_batched": ([_P, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_global_scale_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_global_scale": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
@@ -127,13 +128,25 @@ def nvfp4_global_scale_workspace_size(batch: int, out: int, inp: int) -> int:
 
 
 def nvfp4_diag_hessian(X, tokens, inp, ldx, h_acc, h, accumulate, workspace, stream=None, prepare=False):
-    _need(h_acc, inp, "h_acc")
+    """h_acc = h = None: deferred mode (row-group sums into the workspace only)."""
+    if h_acc is not None:
+        _need(h_acc, inp, "h_acc")
     if h is not None:
         _need(h, inp, "h")
     return _run("nvfp4_diag_hessian", (
         _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx,
         _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), prepare)
+
+
+def nvfp4_diag_hessian_finalize(X_dtype, tokens, inp, h_acc, h, accumulate, workspace,
+                                stream=None, prepare=False):
+    """Finalize of deferred nvfp4_diag_hessian calls (X_dtype: torch.bfloat16 or float32)."""
+    dt = DTYPE_BF16 if X_dtype == torch.bfloat16 else DTYPE_F32
+    return _run("nvfp4_diag_hessian_finalize", (
+        dt, tokens, inp, _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)),
+        int(accumulate), _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
         _stream(stream)), prepare)
 
 

@@ -81,12 +81,26 @@ const char* nvfp4_version(void);
  * Requires in % 8 == 0 and ldx % 8 == 0. tokens == 0 is valid: h_acc is cleared (accumulate
  * == 0) or kept, and h is written from it. Partial sums are combined in a fixed order, so the
  * result does not depend on scheduling.
+ *
+ * Deferred mode, for token chunks of one calibration set: with h_acc == NULL and h == NULL the
+ * call only adds the chunk's binary64 row-group sums into the workspace (replacing them when
+ * accumulate == 0), and nvfp4_diag_hessian_finalize later turns the workspace into h_acc and
+ * h. One finalize per set instead of one per chunk. Every call of a sequence uses the same
+ * workspace, x_dtype and in; the first call has accumulate == 0 and the largest token count
+ * of the sequence, which finalize is given as `tokens` (it fixes the workspace layout).
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_diag_hessian_workspace_size(int64_t tokens, int64_t in, int64_t segments);
 
 nvfp4_status nvfp4_diag_hessian(const void* X, int x_dtype, int64_t tokens, int64_t in,
                                 int64_t ldx, double* h_acc, float* h, int accumulate,
                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Finalize of a deferred sequence of nvfp4_diag_hessian calls: h_acc[j] = (accumulate ?
+ * h_acc[j] : 0) + the binary64 sum of the workspace's row-group slots, h[j] = (float) h_acc[j]
+ * (h may be NULL). tokens and x_dtype are those of the sequence's first call. */
+nvfp4_status nvfp4_diag_hessian_finalize(int x_dtype, int64_t tokens, int64_t in, double* h_acc,
+                                         float* h, int accumulate, void* workspace,
+                                         size_t workspace_bytes, void* stream);
 
 /* Batched form for a mixture-of-experts layer: X holds the routed tokens of `segments` experts
  * back to back; expert e owns rows [seg_offsets[e], seg_offsets[e+1]). Writes h_acc/h as

@@ -25,7 +25,7 @@ def test_header_declares_the_boundary():
                  "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
                  "nvfp4_output_error", "nvfp4_output_error_workspace_size",
                  "nvfp4_quantize_activations", "nvfp4_quantize_activations_workspace_size",
-                 "nvfp4_status_string",
+                 "nvfp4_diag_hessian_finalize", "nvfp4_status_string",
                  "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
         assert want in names
 
@@ -164,6 +164,20 @@ def test_quantize_activations_rejects_bad_arguments(lib):
     assert call(X=ODD) == n.ERR_ALIGN
     assert call(wsb=need - 1) == n.ERR_WORKSPACE
     assert call(T=0, X=None) == n.OK
+
+
+def test_hessian_finalize_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    f = lib.nvfp4_diag_hessian_finalize
+    need = lib.nvfp4_diag_hessian_workspace_size(1000, 64, 1)
+    assert f(5, 1000, 64, FAKE, None, 0, FAKE, need, None) == n.ERR_DTYPE
+    assert f(1, 1000, 60, FAKE, None, 0, FAKE, need, None) == n.ERR_SHAPE
+    assert f(1, 1000, 64, None, None, 0, FAKE, need, None) == n.ERR_NULL
+    assert f(1, 1000, 64, ODD, None, 0, FAKE, need, None) == n.ERR_ALIGN
+    assert f(1, 1000, 64, FAKE, None, 0, FAKE, need - 8, None) == n.ERR_WORKSPACE
+    # deferred partial pass: no outputs, but a workspace is needed
+    H = lib.nvfp4_diag_hessian
+    assert H(FAKE, 1, 1000, 64, 64, None, None, 0, None, 0, None) == n.ERR_WORKSPACE
 
 
 def test_pack_and_global_scale_reject_bad_arguments(lib):

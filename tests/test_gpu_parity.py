@@ -360,3 +360,30 @@ def test_empty_inputs(nv):
     assert S.item() == 1.0
     r = nv.scale_search(W, torch.ones(64, device=DEV), S, nv.WMSE)
     assert r["scales"].numel() == 0
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_hessian_deferred_chunks(nv, dtype):
+    """Deferred mode: chunks only add row-group sums into the workspace (a shorter last
+    chunk included), one finalize at the end; equal to the oracle over all tokens, and a
+    second finalize with accumulate adds the same sums again."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(77)
+    inp = 1040
+    sizes = [3000, 3000, 3000, 1234]
+    chunks = [(torch.randn((t, inp), generator=g, device=DEV) *
+               torch.exp(torch.randn(inp, generator=g, device=DEV))).to(dtype) for t in sizes]
+    T0 = sizes[0]
+    ws = torch.empty(nv.nvfp4_diag_hessian_workspace_size(T0, inp, 1), dtype=torch.uint8, device=DEV)
+    for i, X in enumerate(chunks):
+        nv.nvfp4_diag_hessian(X, X.shape[0], inp, inp, None, None, i > 0, ws)
+    h_acc = torch.empty(inp, dtype=torch.float64, device=DEV)
+    h = torch.empty(inp, dtype=torch.float32, device=DEV)
+    nv.nvfp4_diag_hessian_finalize(dtype, T0, inp, h_acc, h, False, ws)
+    torch.cuda.synchronize()
+    acc_o, h_o = oracle.diag_hessian(host_w(torch.cat(chunks)))
+    np.testing.assert_allclose(h_acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    nv.nvfp4_diag_hessian_finalize(dtype, T0, inp, h_acc, None, True, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(h_acc.cpu().numpy(), 2 * acc_o, rtol=1e-12, atol=0)
