@@ -83,6 +83,8 @@ def _load():
     lib.ref_scale_search_proposal.argtypes = [P, I, I64, I64, I64, P, I, I, I, P, P,
                                               ctypes.c_float, P, P, P, P, I]
     lib.ref_scale_search_proposal.restype = I
+    lib.ref_gptq.argtypes = [P, I, I64, I64, I64, P, P, I, I, I, ctypes.c_float, P, P, P, I]
+    lib.ref_gptq.restype = I
     lib.ref_dequant.argtypes = [P, P, I64, I64, ctypes.c_float, P]
     lib.ref_dequant.restype = I
     lib.ref_group_candidates.argtypes = [P, P, ctypes.c_float, I, I, I, P, P]
@@ -241,6 +243,26 @@ def pack(W: np.ndarray, scales: np.ndarray, S: float, threads: int | None = None
     if rc != 0:
         raise ValueError(f"oracle pack failed ({rc})")
     return packed
+
+
+def gptq(W: np.ndarray, U: np.ndarray, h: np.ndarray | None, objective: int, lo: int, hi: int,
+         S: float, threads: int | None = None):
+    """GPTQ with the window search as local quantiser (H-Scale App. B). U: the upper factor of
+    the damped inverse Hessian, float32 [in, in]. Returns scales, packed and the updated
+    binary32 weights W_final."""
+    W = np.ascontiguousarray(W)
+    out, n = W.shape
+    U = np.ascontiguousarray(U, dtype=np.float32)
+    hh = None if h is None else np.ascontiguousarray(h, dtype=np.float32)
+    scales = np.empty((out, n // 16), dtype=np.uint8)
+    packed = np.empty((out, n // 2), dtype=np.uint8)
+    W_final = np.empty((out, n), dtype=np.float32)
+    rc = _load().ref_gptq(_ptr(W), _dtype_code(W), out, n, n, _ptr(U), _ptr(hh), objective, lo,
+                          hi, ctypes.c_float(S), _ptr(scales), _ptr(packed), _ptr(W_final),
+                          threads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle gptq failed ({rc})")
+    return {"scales": scales, "packed": packed, "W_final": W_final}
 
 
 def dequant(packed: np.ndarray, scales: np.ndarray, S: float) -> np.ndarray:

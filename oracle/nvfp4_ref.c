@@ -461,6 +461,78 @@ int ref_pack(const void* W, int dtype, int64_t out, int64_t in, int64_t ldw,
 }
 
 /* ------------------------------------------------------------------------------------------ */
+/* GPTQ with the scale search as its local quantizer ([HS] App. B: the search replaces only   */
+/* the local quantisation call; inverse-Cholesky processing and error propagation are kept;  */
+/* [SR] §3: input columns in sequence with one shared Hessian factor, rows independent).      */
+/* ------------------------------------------------------------------------------------------ */
+
+/* One output row, all binary32, in this order for column j = 0..in-1:
+ *   - at the first column of a 16-column group: the group's scale code c by search_group on
+ *     the row's current values of the group's columns (and their h);
+ *   - x = fl(|w_j| * r[c]), q = E2M1 index with w_j's sign, the dequantised value
+ *     v = fl(level * eff[c]) with the sign, err = fl(fl(w_j - v) / U[j][j]);
+ *   - every later column k > j: w_k = fma(-err, U[j][k], w_k).
+ * U is the upper-triangular factor of the damped inverse Hessian (row-major [in, in]); the
+ * nibble of column j and the group's code are the outputs. w is updated in place. */
+static void gptq_row(float* w, int64_t in, const float* U, const float* h, const float* eff,
+                     const float* rcp, float S, int lo, int hi, uint8_t* scales, uint8_t* packed)
+{
+    int c = 0;
+    for (int64_t j = 0; j < in; ++j) {
+        if (j % 16 == 0) {
+            uint8_t nib_unused[16], sc;
+            float L;
+            int off;
+            search_group(w + j, h ? h + j : NULL, eff, rcp, S, lo, hi, 0, &sc, nib_unused, &L,
+                         &off);
+            c = sc;
+            scales[j / 16] = sc;
+        }
+        float a = fabsf(w[j]);
+        int idx = (c == 0) ? 0 : ref_e2m1_index(a * rcp[c]);
+        float mag = (c == 0) ? 0.0f : E2M1_LEVEL[idx] * eff[c];
+        float v = signbit(w[j]) ? -mag : mag;
+        uint8_t nib = (uint8_t)((signbit(w[j]) ? 8 : 0) | idx);
+        if (j & 1)
+            packed[j / 2] = (uint8_t)(packed[j / 2] | (nib << 4));
+        else
+            packed[j / 2] = nib;
+        float err = (w[j] - v) / U[j * in + j];
+        for (int64_t k = j + 1; k < in; ++k) w[k] = fmaf(-err, U[j * in + k], w[k]);
+    }
+}
+
+/* GPTQ over W[out, in] with the window search as local quantiser. Outputs scales[out, in/16]
+ * and packed[out, in/2]; W_final[out, in] (optional) receives the updated binary32 weights. */
+int ref_gptq(const void* W, int dtype, int64_t out, int64_t in, int64_t ldw, const float* U,
+             const float* h, int objective, int lo, int hi, float S, uint8_t* scales,
+             uint8_t* packed, float* W_final, int nthreads)
+{
+    if (in % 16 != 0 || out < 0 || in < 0 || ldw < in || !U) return REF_ERR_ARG;
+    if (objective == REF_WMSE && !h) return REF_ERR_ARG;
+    if (objective == REF_MSE) h = NULL;
+    if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return REF_ERR_ARG;
+    if (!isfinite(S) || !(S > 0.0f)) return REF_ERR_ARG;
+    float eff[127], rcp[127];
+    if (ref_scale_tables(S, eff, rcp) != REF_OK) return REF_ERR_ARG;
+    if (nthreads < 1) nthreads = 1;
+    int bad = 0;
+#pragma omp parallel for num_threads(nthreads) schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t o = 0; o < out; ++o) {
+        float* w = (float*)malloc((size_t)in * sizeof(float));
+        if (!w) { bad = 1; continue; }
+        for (int64_t i = 0; i < in; ++i) {
+            w[i] = load_elem(W, dtype, o * ldw + i);
+            if (!isfinite(w[i])) bad = 1;
+        }
+        gptq_row(w, in, U, h, eff, rcp, S, lo, hi, scales + o * (in / 16), packed + o * (in / 2));
+        if (W_final) memcpy(W_final + o * in, w, (size_t)in * sizeof(float));
+        free(w);
+    }
+    return bad ? REF_ERR_NONFINITE : REF_OK;
+}
+
+/* ------------------------------------------------------------------------------------------ */
 /* Layer-output evaluation ([HS] §3: layer-output reconstruction; the activation-loss         */
 /* comparison of Min-Max, MSE-guided and Hessian-guided scales).                             */
 /* ------------------------------------------------------------------------------------------ */
