@@ -51,6 +51,7 @@ FLOPS_PER_ELEM_CAND = {"wmse": 7, "mse": 6}
 
 METRIC = "weights/s and HBM GB/s (fraction of peak) for scale search+pack; h-reduce GB/s"
 KERNEL_SOURCES = ["block_scale_search_amd/csrc/scale_search.hip",
+                  "block_scale_search_amd/csrc/search_device.h",
                   "block_scale_search_amd/csrc/device_formats.h"]
 
 
@@ -311,6 +312,10 @@ def main():
     ap.add_argument("--activations", action="store_true",
                     help="also time on-line activation quantisation (dynamic S + MSE [-3,7]) of "
                          "the first token chunk and of a 16-token decode batch, outside the step")
+    ap.add_argument("--gptq", action="store_true",
+                    help="also time GPTQ with the window search as local quantiser on the first "
+                         "layer (U from X^T X of the first token chunk, 1%% damping), outside "
+                         "the step")
     ap.add_argument("--output-error", action="store_true",
                     help="also time the layer-output error evaluation (MFMA) of the last mode's "
                          "codes over the first token chunk, outside the step")
@@ -482,6 +487,44 @@ def main():
                           "GB/s": round(nbytes / us1 / 1e3, 1),
                           "weights/s": Ta * na / (us1 * 1e-6)}
 
+    # GPTQ (outside the step): the damped inverse-Hessian factor is caller-side preparation
+    # (binary64 Gram matrix, inverse and Cholesky), untimed; the library call is timed
+    gq = None
+    if args.gptq and cfg.batch == 1:
+        from block_scale_search_amd import workloads as workloads_mod
+        s0 = runner.sets[0]
+        Xd = s0.chunks[0].double()
+        H = Xd.T @ Xd
+        H += 0.01 * torch.diagonal(H).mean() * torch.eye(cfg.inp, dtype=torch.float64, device=dev)
+        Ud = torch.linalg.cholesky(torch.cholesky_inverse(torch.linalg.cholesky(H))).T.contiguous()
+        U = Ud.float().contiguous()
+        hd = torch.diagonal(H).float().contiguous()
+        del Xd, H, Ud
+        m = next((mm for mm in cfg.modes if mm.objective == "wmse" and not mm.exhaustive
+                  and not mm.proposal), None) or workloads_mod.Mode("wmse", -9, 6)
+        sc = torch.empty((cfg.out, cfg.inp // 16), dtype=torch.uint8, device=dev)
+        pk = torch.empty((cfg.out, cfg.inp // 2), dtype=torch.uint8, device=dev)
+        wsq = torch.empty(nv.nvfp4_gptq_workspace_size(cfg.out, cfg.inp), dtype=torch.uint8,
+                          device=dev)
+        call = nv.nvfp4_gptq(s0.W, cfg.out, cfg.inp, cfg.inp, U, hd, nv.WMSE, m.lo, m.hi, s0.S,
+                             sc, pk, None, wsq, prepare=True)
+        call()
+        torch.cuda.synchronize()
+        reps = 3
+        p0.record(main)
+        for _ in range(reps):
+            call()
+        p1.record(main)
+        torch.cuda.synchronize()
+        g_us = p0.elapsed_time(p1) * 1e3 / reps
+        n_fma = cfg.out * cfg.inp * (cfg.inp - 1) / 2
+        search_ops = cfg.out * cfg.inp * n_candidates(m) * OPS_PER_ELEM_CAND["wmse"]
+        gq = {"ms": round(g_us / 1e3, 3), "mode": f"WMSE [{m.lo},{m.hi}]",
+              "ordered_fmas": n_fma, "search_lane_ops": search_ops,
+              "TOP/s": round((n_fma + search_ops) / g_us / 1e6, 2),
+              "frac_valu_issue": round((n_fma + search_ops) / g_us / 1e6 / VALU_PEAK_TOPS, 4),
+              "weights/s": cfg.out * cfg.inp / (g_us * 1e-6)}
+
     per_label = {}
     for row in ev:
         for lab, (e0, e1) in zip(labels, row):
@@ -573,6 +616,8 @@ def main():
         line["output_error"] = oe
     if acts is not None:
         line["activations"] = acts
+    if gq is not None:
+        line["gptq"] = gq
     print(json.dumps(line), flush=True)
 
 

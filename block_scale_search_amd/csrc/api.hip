@@ -288,6 +288,36 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
                                                  nullptr, s));
 }
 
+size_t nvfp4_gptq_workspace_size(int64_t out, int64_t in) {
+    if (out < 0 || in < 0) return 0;
+    return nvfp4::gptq_workspace_bytes(out, in);
+}
+
+nvfp4_status nvfp4_gptq(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                        const float* U, const float* h, int objective, int32_t lo, int32_t hi,
+                        const float* S, uint8_t* scales, uint8_t* packed, float* W_final,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
+    if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return NVFP4_ERR_WINDOW;
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    if (st != NVFP4_OK) return st;
+    if (out * in >= ((int64_t)1 << 39)) return NVFP4_ERR_SHAPE;
+    if (out == 0 || in == 0) return NVFP4_OK;
+    const bool wmse = objective == NVFP4_WMSE;
+    if (U == nullptr || S == nullptr || scales == nullptr || packed == nullptr ||
+        (wmse && h == nullptr))
+        return NVFP4_ERR_NULL;
+    if (!aligned16(U) || (reinterpret_cast<uintptr_t>(S) & 3u) || !aligned8(packed) ||
+        (h && (reinterpret_cast<uintptr_t>(h) & 3u)) || (W_final && !aligned16(W_final)))
+        return NVFP4_ERR_ALIGN;
+    const size_t need = nvfp4::gptq_workspace_bytes(out, in);
+    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_gptq(W, w_dtype == NVFP4_DTYPE_BF16, out, in, ldw, U,
+                                         wmse ? h : nullptr, wmse, lo, hi, S, scales, packed,
+                                         W_final, workspace, static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in) {
     if (tokens < 0 || out < 0 || in < 0) return 0;
     return nvfp4::output_error_workspace_bytes(tokens, out, in);

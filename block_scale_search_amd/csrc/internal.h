@@ -68,6 +68,14 @@ hipError_t launch_output_error(const void* X, int64_t tokens, int64_t in, int64_
                                const uint8_t* scales, const uint8_t* packed, const float* S,
                                double* err, bool accumulate, void* workspace, hipStream_t stream);
 
+// GPTQ with the window search as local quantiser: workspace bytes and launch (W_final may be
+// NULL; the binary32 working copy then lives in the workspace).
+size_t gptq_workspace_bytes(int64_t out, int64_t in);
+hipError_t launch_gptq(const void* W, bool bf16, int64_t out, int64_t in, int64_t ldw,
+                       const float* U, const float* h, bool wmse, int lo, int hi, const float* S,
+                       uint8_t* scales, uint8_t* packed, float* W_final, void* workspace,
+                       hipStream_t stream);
+
 hipError_t launch_pack(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                        int64_t ldw, int64_t stride_w, const uint8_t* scales, const float* S,
                        uint8_t* packed, hipStream_t stream);

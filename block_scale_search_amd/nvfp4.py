@@ -46,6 +46,9 @@ _SIGS = {
     "nvfp4_quantize_activations_workspace_size": ([_I64, _I64], _SZ),
     "nvfp4_quantize_activations": ([_P, _I, _I64, _I64, _I64, _I, _P, _I32, _I32, _I, _P, _P, _P,
                                     _P, _SZ, _P], _I),
+    "nvfp4_gptq_workspace_size": ([_I64, _I64], _SZ),
+    "nvfp4_gptq": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
+                    _P], _I),
     "nvfp4_output_error_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_output_error": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _I64, _P, _P, _P, _P, _I,
                             _P, _SZ, _P], _I),
@@ -239,6 +242,24 @@ def nvfp4_quantize_activations(X, tokens, inp, ldx, objective, h, lo, hi, rule, 
         _stream(stream)), prepare)
 
 
+def nvfp4_gptq_workspace_size(out: int, inp: int) -> int:
+    return int(_lib.nvfp4_gptq_workspace_size(out, inp))
+
+
+def nvfp4_gptq(W, out, inp, ldw, U, h, objective, lo, hi, S, scales, packed, W_final, workspace,
+               stream=None, prepare=False):
+    _need(scales, out * (inp // 16), "scales")
+    _need(packed, out * (inp // 2), "packed")
+    _need(U, inp * inp, "U")
+    return _run("nvfp4_gptq", (
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), out, inp, ldw,
+        _dev(U, "U", (torch.float32,)), _dev(h, "h", (torch.float32,)), objective, lo, hi,
+        _dev(S, "S", (torch.float32,)), _dev(scales, "scales", (torch.uint8,)),
+        _dev(packed, "packed", (torch.uint8,)), _dev(W_final, "W_final", (torch.float32,)),
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), prepare)
+
+
 def nvfp4_output_error_workspace_size(tokens: int, out: int, inp: int) -> int:
     return int(_lib.nvfp4_output_error_workspace_size(tokens, out, inp))
 
@@ -371,6 +392,23 @@ def quantize_activations(X: torch.Tensor, objective: int = MSE, lo: int = -3, hi
     nvfp4_quantize_activations(X, T, n, X.stride(0), objective, h if objective == WMSE else None,
                                lo, hi, rule, S, scales, packed, ws, stream)
     return {"S": S, "scales": scales, "packed": packed}
+
+
+def gptq(W: torch.Tensor, U: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor,
+         objective: int = WMSE, lo: int = -9, hi: int = 6, with_final: bool = False, stream=None):
+    """GPTQ over W [out, in] with the window search as local quantiser (U: upper factor of the
+    damped inverse Hessian, float32 [in, in])."""
+    o, n = W.shape
+    if W.stride(1) != 1:
+        raise ValueError("W rows must be contiguous")
+    dev = W.device
+    scales = torch.empty((o, n // 16), dtype=torch.uint8, device=dev)
+    packed = torch.empty((o, n // 2), dtype=torch.uint8, device=dev)
+    W_final = torch.empty((o, n), dtype=torch.float32, device=dev) if with_final else None
+    ws = torch.empty(max(16, nvfp4_gptq_workspace_size(o, n)), dtype=torch.uint8, device=dev)
+    nvfp4_gptq(W, o, n, W.stride(0), U.contiguous(), h if objective == WMSE else None, objective,
+               lo, hi, S, scales, packed, W_final, ws, stream)
+    return {"scales": scales, "packed": packed, "W_final": W_final}
 
 
 def output_error(X: torch.Tensor, W: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

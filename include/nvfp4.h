@@ -209,6 +209,41 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
                         uint8_t* packed, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * GPTQ with the scale search as local quantiser ([HS] App. B: the search replaces only GPTQ's
+ * local quantisation call, and inverse-Cholesky processing and error propagation are kept;
+ * [SR] §3: input columns in sequence with one shared Hessian factor, output rows independent).
+ *
+ * For every row o and column j = 0..in-1 in order, all in binary32:
+ *   - at the first column of each 16-column group the group's scale code is chosen as by
+ *     nvfp4_scale_search (window lo..hi around the base code, lowest code on ties), from the
+ *     row's current (already updated) values of the group's columns and their h;
+ *   - the column is quantised at that code (signed E2M1 code of fl(w_j * r[c])), its
+ *     dequantised value v = fl(level * eff[c]) with w_j's sign, err = fl(fl(w_j - v) / U[j][j]);
+ *   - every later column k > j takes w_k = fma(-err, U[j][k], w_k), in column order j.
+ * Each element receives exactly this sequence of operations whatever the internal blocking, so
+ * results are deterministic and reproducible by a sequential implementation.
+ *
+ * W         device, bf16 or f32 [out, in], row stride ldw (16-byte aligned rows).
+ * U         device float [in, in] row-major, 16-byte aligned: the upper-triangular factor of the
+ *           damped inverse Hessian, (H + damping)^-1 = U^T U (entries below the diagonal are not
+ *           read); computed by the caller, e.g. with a Cholesky routine.
+ * h         device float [in], the diagonal weights of the search (WMSE), e.g. diag(H); NULL
+ *           for MSE.
+ * S         device float [1]: the global scale (e.g. from nvfp4_global_scale on W).
+ * scales    device uint8 [out, in/16]; packed device uint8 [out, in/2], 8-byte aligned.
+ * W_final   device float [out, in] or NULL (16-byte aligned): receives the updated binary32
+ *           weights.
+ * workspace device, nvfp4_gptq_workspace_size(out, in) bytes, 16-byte aligned, no
+ *           initialisation needed.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_gptq_workspace_size(int64_t out, int64_t in);
+
+nvfp4_status nvfp4_gptq(const void* W, int w_dtype, int64_t out, int64_t in, int64_t ldw,
+                        const float* U, const float* h, int objective, int32_t lo, int32_t hi,
+                        const float* S, uint8_t* scales, uint8_t* packed, float* W_final,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * On-line activation quantisation ([SS] Experimental Results: the WA, WAKV and WAKVQ settings
  * quantise activations, KV cache and query states with the same sweep; [SS] §2: the per-tensor
  * global scale S = max|x| / (256 * 6)).

@@ -25,7 +25,8 @@ def test_header_declares_the_boundary():
                  "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
                  "nvfp4_output_error", "nvfp4_output_error_workspace_size",
                  "nvfp4_quantize_activations", "nvfp4_quantize_activations_workspace_size",
-                 "nvfp4_diag_hessian_finalize", "nvfp4_status_string",
+                 "nvfp4_diag_hessian_finalize", "nvfp4_gptq", "nvfp4_gptq_workspace_size",
+                 "nvfp4_status_string",
                  "nvfp4_diag_hessian_workspace_size", "nvfp4_global_scale_workspace_size"):
         assert want in names
 
@@ -178,6 +179,29 @@ def test_hessian_finalize_rejects_bad_arguments(lib):
     # deferred partial pass: no outputs, but a workspace is needed
     H = lib.nvfp4_diag_hessian
     assert H(FAKE, 1, 1000, 64, 64, None, None, 0, None, 0, None) == n.ERR_WORKSPACE
+
+
+def test_gptq_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    need = lib.nvfp4_gptq_workspace_size(4, 64)
+
+    def call(**kw):
+        a = dict(W=FAKE, wd=1, out=4, inp=64, ldw=64, U=FAKE, h=FAKE, obj=1, lo=-9, hi=6, S=FAKE,
+                 sc=FAKE, pk=FAKE, wf=None, ws=FAKE, wsb=need)
+        a.update(kw)
+        return lib.nvfp4_gptq(a["W"], a["wd"], a["out"], a["inp"], a["ldw"], a["U"], a["h"],
+                              a["obj"], a["lo"], a["hi"], a["S"], a["sc"], a["pk"], a["wf"],
+                              a["ws"], a["wsb"], None)
+    assert call(obj=2) == n.ERR_ARG
+    assert call(lo=1) == n.ERR_WINDOW
+    assert call(inp=40, ldw=40) == n.ERR_SHAPE
+    assert call(U=None) == n.ERR_NULL
+    assert call(h=None) == n.ERR_NULL                             # WMSE needs h
+    assert call(W=ODD) == n.ERR_ALIGN
+    assert call(U=ctypes.c_void_p((1 << 20) + 8)) == n.ERR_ALIGN        # U needs 16 bytes
+    assert call(wf=ctypes.c_void_p((1 << 20) + 4)) == n.ERR_ALIGN       # so does W_final
+    assert call(wsb=need - 4) == n.ERR_WORKSPACE
+    assert call(out=0) == n.OK
 
 
 def test_pack_and_global_scale_reject_bad_arguments(lib):
