@@ -3,6 +3,8 @@
 One step = the whole path over one synthetic layer held in HBM:
   diagonal Hessian over X -> global scale of W -> scale search + pack for every mode the
   workload names (attn8b: MSE [-3,7] and WMSE [-8,7]).
+On workloads of one matrix and one token chunk, h and S come from one call
+(nvfp4_layer_statistics, two launches; --separate-stats times the two separate calls).
 With --streams 2 the h-reduce runs on a second stream (same default priority), overlapping the
 global scale and the searches that do not read h; the searches that read h wait for it. The
 default is one stream, so that every kernel's time is its own.
@@ -109,6 +111,9 @@ class Runner:
                                 dtype=torch.uint8, device=dev)
         self.ws_s = torch.zeros(max(1, nvfp4.nvfp4_global_scale_workspace_size(E, cfg.out, cfg.inp)),
                                 dtype=torch.uint8, device=dev)
+        self.ws_ls = torch.zeros(max(16, nvfp4.nvfp4_layer_statistics_workspace_size(
+            T, cfg.inp, cfg.out)), dtype=torch.uint8, device=dev)
+        self.separate_stats = False
         self.rule = nvfp4.GS_AMAX_256 if cfg.gs_rule == "amax256" else nvfp4.GS_AMAX_448
         if any(m.proposal for m in cfg.modes):
             # proposal and incoming codes, made once outside the timed steps: the incoming code is
@@ -134,7 +139,14 @@ class Runner:
         import torch
         hs = aux if aux is not None else torch.cuda.current_stream()
         deferred = len(s.chunks) > 1 and s.seg is None
-        for ci, X in enumerate(s.chunks):
+        # one matrix, one token chunk, one stream: h and S in one call (two launches)
+        fused = aux is None and s.seg is None and len(s.chunks) == 1 and not self.separate_stats
+        if fused:
+            X = s.chunks[0]
+            out.append(("h_reduce+global_scale", nv.nvfp4_layer_statistics(
+                X, X.shape[0], n, n, s.h_acc, s.h, False, s.W, o, ldw, self.rule, s.S,
+                self.ws_ls, prepare=True), "main"))
+        for ci, X in enumerate(s.chunks if not fused else []):
             T = X.shape[0]
             if s.seg is not None:
                 out.append(("h_reduce", nv.nvfp4_diag_hessian_batched(
@@ -154,8 +166,9 @@ class Runner:
             out.append(("h_finalize", nv.nvfp4_diag_hessian_finalize(
                 s.chunks[0].dtype, s.chunks[0].shape[0], n, s.h_acc, s.h, False, self.ws_h,
                 stream=hs, prepare=True), "aux"))
-        out.append(("global_scale", nv.nvfp4_global_scale(
-            s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
+        if not fused:
+            out.append(("global_scale", nv.nvfp4_global_scale(
+                s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
         for mi, m in enumerate(cfg.modes):
             wm = m.objective == "wmse"
             if m.proposal:
@@ -193,6 +206,9 @@ def algorithmic(cfg, label: str):
         return T * cfg.inp * 2 + cfg.batch * cfg.inp * 12, 2 * T * cfg.inp
     if label == "global_scale":
         return n_w * wb + 4 * cfg.batch, n_w
+    if label == "h_reduce+global_scale":
+        T = cfg.chunk_tokens or cfg.tokens
+        return T * cfg.inp * 2 + cfg.inp * 12 + n_w * wb + 4, 2 * T * cfg.inp + n_w
     mode = next(m for m in cfg.modes if label == f"search:{m.label}")
     bytes_ = n_w * wb + n_w // 2 + n_w // 16 + (cfg.batch * cfg.inp * 4 if mode.objective == "wmse" else 0)
     if mode.proposal:
@@ -302,6 +318,9 @@ def main():
     ap.add_argument("--workload", default="attn8b")
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = enough for >1 GB)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--separate-stats", action="store_true",
+                    help="h and S as two calls (nvfp4_diag_hessian, nvfp4_global_scale) instead "
+                         "of nvfp4_layer_statistics on one-chunk workloads")
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: h-reduce on a second stream, overlapping the global scale and the "
                          "searches that do not read h")
@@ -336,6 +355,7 @@ def main():
     print(f"# workload {cfg.name}: {cfg.description}; {n_sets} input set(s)", file=sys.stderr,
           flush=True)
     runner = Runner(cfg, n_sets, dev)
+    runner.separate_stats = args.separate_stats
     torch.cuda.synchronize()
 
     if args.calib_copy:
@@ -579,15 +599,24 @@ def main():
         threads = min(16, len(os.sched_getaffinity(0)))
         cpu = cpu_baseline(cfg, runner.sets[0], threads)
 
-    # the h stage of a step: every chunk's call plus the deferred finalize, over X's bytes
-    h_us = kernels["h_reduce"]["avg_us"] * kernels["h_reduce"]["calls_per_step"]
-    if "h_finalize" in kernels:
-        h_us += kernels["h_finalize"]["avg_us"]
+    # the h stage of a step: every chunk's call plus the deferred finalize, over X's bytes; with
+    # the fused call, h and S together over the bytes of X and W
     x_bytes = cfg.tokens * cfg.inp * 2
-    h_stage_gbs = round(x_bytes / h_us / 1e3, 1)
-    kernels["h_stage (all chunks + finalize)"] = {
-        "us_per_step": round(h_us, 2), "x_bytes": x_bytes, "GB/s": h_stage_gbs,
-        "frac_hbm": round(h_stage_gbs / HBM_PEAK_GBS, 4)}
+    if "h_reduce+global_scale" in kernels:
+        h_us = kernels["h_reduce+global_scale"]["avg_us"]
+        st_bytes = algorithmic(cfg, "h_reduce+global_scale")[0]
+        h_stage_gbs = round(st_bytes / h_us / 1e3, 1)
+        kernels["h+S stage (one call, X and W bytes)"] = {
+            "us_per_step": round(h_us, 2), "bytes": st_bytes, "GB/s": h_stage_gbs,
+            "frac_hbm": round(h_stage_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        h_us = kernels["h_reduce"]["avg_us"] * kernels["h_reduce"]["calls_per_step"]
+        if "h_finalize" in kernels:
+            h_us += kernels["h_finalize"]["avg_us"]
+        h_stage_gbs = round(x_bytes / h_us / 1e3, 1)
+        kernels["h_stage (all chunks + finalize)"] = {
+            "us_per_step": round(h_us, 2), "x_bytes": x_bytes, "GB/s": h_stage_gbs,
+            "frac_hbm": round(h_stage_gbs / HBM_PEAK_GBS, 4)}
 
     searched = cfg.n_weights * len(cfg.modes)
     line = {
@@ -610,7 +639,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
-        "h_reduce_GB/s": h_stage_gbs,
+        "h_reduce_GB/s" if "h_reduce" in kernels else "h_and_global_scale_GB/s": h_stage_gbs,
     }
     if oe is not None:
         line["output_error"] = oe

@@ -163,6 +163,41 @@ nvfp4_status nvfp4_global_scale(const void* W, int w_dtype, int64_t batch, int64
                                                  static_cast<hipStream_t>(stream)));
 }
 
+size_t nvfp4_layer_statistics_workspace_size(int64_t tokens, int64_t in, int64_t out) {
+    if (tokens < 0 || in < 0 || out < 0) return 0;
+    return nvfp4::layer_statistics_workspace_bytes(tokens, in, out);
+}
+
+nvfp4_status nvfp4_layer_statistics(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                    int64_t ldx, double* h_acc, float* h, int accumulate,
+                                    const void* W, int w_dtype, int64_t out, int64_t ldw, int rule,
+                                    float* S, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    if (elem_size(x_dtype) == 0) return NVFP4_ERR_DTYPE;
+    if (tokens < 0 || in < 0 || out < 0) return NVFP4_ERR_SHAPE;
+    if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    if (st != NVFP4_OK) return st;
+    if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
+    if (in == 0) return NVFP4_OK;
+    if (h_acc == nullptr || S == nullptr) return NVFP4_ERR_NULL;
+    if (tokens > 0 && X == nullptr) return NVFP4_ERR_NULL;
+    if ((X && !aligned16(X)) || !aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u)) ||
+        (reinterpret_cast<uintptr_t>(S) & 3u))
+        return NVFP4_ERR_ALIGN;
+    if (nvfp4::hessian_launch_blocks(tokens, in, 1, x_dtype == NVFP4_DTYPE_BF16) +
+            nvfp4::amax_partial_count(1, out, in) >=
+        ((int64_t)1 << 31))
+        return NVFP4_ERR_SHAPE;
+    const size_t need = nvfp4::layer_statistics_workspace_bytes(tokens, in, out);
+    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_layer_statistics(
+        X, x_dtype == NVFP4_DTYPE_BF16, tokens, in, ldx, h_acc, h, accumulate != 0, W,
+        w_dtype == NVFP4_DTYPE_BF16, out, ldw, rule, S, workspace,
+        static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64_t out,
                                 int64_t in, int64_t ldw, int64_t stride_w, int32_t group_size,
                                 const float* h, int64_t stride_h, int objective, int32_t lo,

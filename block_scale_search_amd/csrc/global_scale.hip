@@ -12,43 +12,15 @@
 // HBM traffic: W once plus 4 B per workgroup.
 #include <hip/hip_runtime.h>
 
+#include "amax_device.h"
 #include "internal.h"
 
 namespace nvfp4 {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kLoads = 4;
 constexpr int kTargetBlocks = 512;          // workgroups per launch, over all matrices
-constexpr int64_t kMinChunk = kThreads * kLoads;  // vectors per workgroup at least
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-template <bool BF16>
-__device__ __forceinline__ uint32_t absmax_bits(const uint4 d) {
-    if constexpr (BF16) {
-        const uint32_t x[4] = {d.x & 0x7FFF7FFFu, d.y & 0x7FFF7FFFu, d.z & 0x7FFF7FFFu,
-                               d.w & 0x7FFF7FFFu};
-        uint32_t m = 0u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = max(m, max(x[i] << 16, x[i] & 0xFFFF0000u));
-        return m;
-    } else {
-        return max(max(d.x & 0x7FFFFFFFu, d.y & 0x7FFFFFFFu),
-                   max(d.z & 0x7FFFFFFFu, d.w & 0x7FFFFFFFu));
-    }
-}
-
-__device__ __forceinline__ uint32_t block_max(uint32_t m, uint32_t* wmax) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    uint32_t r = wmax[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) r = max(r, wmax[i]);
-    return r;
-}
+constexpr int64_t kMinChunk = kThreads * kAmaxLoads;  // vectors per workgroup at least
 
 // Workgroup (x, batch) reduces 16-byte vectors [x * chunk, (x + 1) * chunk) of its matrix,
 // numbered row-major over the `in` columns (vpr vectors per row).
@@ -60,28 +32,8 @@ __global__ __launch_bounds__(kThreads) void k_amax_partial(const uint8_t* __rest
                                                            uint32_t* __restrict__ partial) {
     __shared__ uint32_t wmax[kThreads / 64];
     const int64_t batch = blockIdx.y;
-    const uint8_t* base = W + batch * stride_w_bytes;
-    const bool dense = ldw_bytes == vpr * 16;
-    const int64_t nvec = out * vpr;
-    const int64_t v_begin = (int64_t)blockIdx.x * chunk;
-    const int64_t v_end = min(nvec, v_begin + chunk);
-    uint32_t m = 0u;
-    for (int64_t v0 = v_begin + threadIdx.x; v0 < v_end; v0 += kLoads * kThreads) {
-        uint4 d[kLoads];
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-            const int64_t v = v0 + k * kThreads;
-            d[k] = make_uint4(0u, 0u, 0u, 0u);
-            if (v < v_end) {
-                const int64_t off = dense ? v * 16 : (v / vpr) * ldw_bytes + (v % vpr) * 16;
-                const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + off));
-                d[k] = make_uint4(t.x, t.y, t.z, t.w);
-            }
-        }
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) m = max(m, absmax_bits<BF16>(d[k]));
-    }
-    m = block_max(m, wmax);
+    const uint32_t m = amax_chunk<BF16, kThreads>(W + batch * stride_w_bytes, out, vpr, ldw_bytes,
+                                                  chunk, blockIdx.x, wmax);
     if (threadIdx.x == 0) partial[batch * gridDim.x + blockIdx.x] = m;
 }
 
@@ -89,13 +41,8 @@ __global__ __launch_bounds__(kThreads) void k_global_scale_finalize(
     const uint32_t* __restrict__ partial, int64_t nblk, int rule, float* __restrict__ S) {
     __shared__ uint32_t wmax[kThreads / 64];
     const int64_t batch = blockIdx.x;
-    uint32_t r = 0u;
-    for (int64_t i = threadIdx.x; i < nblk; i += kThreads) r = max(r, partial[batch * nblk + i]);
-    r = block_max(r, wmax);
-    if (threadIdx.x == 0) {
-        const float amax = __uint_as_float(r);
-        S[batch] = amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
-    }
+    const float s = scale_from_amax_partials<kThreads>(partial + batch * nblk, nblk, rule, wmax);
+    if (threadIdx.x == 0) S[batch] = s;
 }
 
 // Workgroups per matrix: about kTargetBlocks over the batch, each with at least kMinChunk
@@ -119,16 +66,23 @@ int64_t amax_partial_count(int64_t batch, int64_t out, int64_t in) {
     return amax_blocks(batch, out, in);
 }
 
+AmaxPlan amax_plan(int64_t batch, int64_t out, int64_t in, bool bf16) {
+    AmaxPlan p;
+    p.nblk = amax_blocks(batch, out, in);
+    p.vpr = in / (bf16 ? 8 : 4);
+    // chunk: whole 4 KB runs of 256 vectors, so every workgroup starts on a 4 KB boundary of a
+    // dense matrix
+    const int64_t chunk = (out * p.vpr + p.nblk - 1) / p.nblk;
+    p.chunk = (chunk + 255) / 256 * 256;
+    return p;
+}
+
 hipError_t launch_amax_partial(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, uint32_t* partial,
                                hipStream_t stream) {
-    const int64_t nblk = amax_blocks(batch, out, in);
+    const AmaxPlan p = amax_plan(batch, out, in, bf16);
+    const int64_t nblk = p.nblk, vpr = p.vpr, chunk = p.chunk;
     const int esz = bf16 ? 2 : 4;
-    const int64_t vpr = in / (bf16 ? 8 : 4);
-    // chunk: whole 4 KB wave-rows of vectors, so every workgroup starts on a 4 KB boundary of a
-    // dense matrix
-    int64_t chunk = (out * vpr + nblk - 1) / nblk;
-    chunk = (chunk + kThreads - 1) / kThreads * kThreads;
     const dim3 grid((uint32_t)nblk, (uint32_t)batch);
     if (bf16)
         hipLaunchKernelGGL(k_amax_partial<true>, grid, dim3(kThreads), 0, stream,

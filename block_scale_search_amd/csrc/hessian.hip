@@ -22,6 +22,7 @@
 // HBM traffic: X once plus 16 B per column per row group (partial written and read back).
 #include <hip/hip_runtime.h>
 
+#include "amax_device.h"
 #include "device_formats.h"
 #include "internal.h"
 
@@ -121,16 +122,16 @@ __global__ __launch_bounds__(256) void k_hess_group_prefix(const int64_t* __rest
 // add != 0: the partial is added to the slot's previous value (deferred accumulation over
 // token chunks) instead of replacing it.
 template <bool BF16, int V>
-__global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restrict__ X,
-                                                         int64_t in, int64_t ldx_bytes,
-                                                         GroupMap map, int64_t n_strips,
-                                                         double* __restrict__ partial, int add) {
+__device__ __forceinline__ void hess_partial_body(const uint8_t* __restrict__ X, int64_t in,
+                                                  int64_t ldx_bytes, const GroupMap& map,
+                                                  int64_t n_strips, double* __restrict__ partial,
+                                                  int add, int64_t blk,
+                                                  double (*red)[XCols<BF16>::kStrip]) {
     constexpr int C = XCols<BF16>::kCols;
     constexpr int SW = XCols<BF16>::kStrip;
-    __shared__ double red[V][SW];
 
-    const int64_t strip = blockIdx.x % n_strips;
-    const int64_t grp = blockIdx.x / n_strips;
+    const int64_t strip = blk % n_strips;
+    const int64_t grp = blk / n_strips;
     int64_t e, row0, row1, g, count;
     if (!map_group(map, grp, e, row0, row1, g, count)) return;  // uniform per workgroup
 
@@ -185,6 +186,15 @@ __global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restri
     }
 }
 
+template <bool BF16, int V>
+__global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restrict__ X,
+                                                         int64_t in, int64_t ldx_bytes,
+                                                         GroupMap map, int64_t n_strips,
+                                                         double* __restrict__ partial, int add) {
+    __shared__ double red[V][XCols<BF16>::kStrip];
+    hess_partial_body<BF16, V>(X, in, ldx_bytes, map, n_strips, partial, add, blockIdx.x, red);
+}
+
 // Eight threads per column: thread `sub` adds row groups sub, sub + 8, ... (8 loads in flight
 // at a time, so up to 64 groups arrive in one round), then the eight sums are combined in sub
 // order.
@@ -192,15 +202,13 @@ constexpr int kFinThreads = 256;
 constexpr int kFinSubs = 8;
 constexpr int kFinCols = kFinThreads / kFinSubs;
 
-__global__ __launch_bounds__(kFinThreads) void k_hess_finalize(const double* __restrict__ partial,
-                                                               int64_t in, GroupMap map,
-                                                               double* __restrict__ h_acc,
-                                                               float* __restrict__ h,
-                                                               int accumulate) {
-    __shared__ double red[kFinSubs][kFinCols];
-    const int64_t e = blockIdx.y;
+__device__ __forceinline__ void hess_finalize_body(const double* __restrict__ partial, int64_t in,
+                                                   const GroupMap& map, double* __restrict__ h_acc,
+                                                   float* __restrict__ h, int accumulate,
+                                                   int64_t blk, int64_t e,
+                                                   double (*red)[kFinCols]) {
     const int cl = threadIdx.x % kFinCols, sub = threadIdx.x / kFinCols;
-    const int64_t c = (int64_t)blockIdx.x * kFinCols + cl;
+    const int64_t c = blk * kFinCols + cl;
     int64_t first = 0, count = groups_for(map.tokens, map.rows_per_group);
     if (map.seg_offsets != nullptr) {
         first = map.group_prefix[e];
@@ -229,6 +237,48 @@ __global__ __launch_bounds__(kFinThreads) void k_hess_finalize(const double* __r
         const double a = (accumulate ? h_acc[idx] : 0.0) + total;
         h_acc[idx] = a;
         if (h) h[idx] = (float)a;
+    }
+}
+
+__global__ __launch_bounds__(kFinThreads) void k_hess_finalize(const double* __restrict__ partial,
+                                                               int64_t in, GroupMap map,
+                                                               double* __restrict__ h_acc,
+                                                               float* __restrict__ h,
+                                                               int accumulate) {
+    __shared__ double red[kFinSubs][kFinCols];
+    hess_finalize_body(partial, in, map, h_acc, h, accumulate, blockIdx.x, blockIdx.y, red);
+}
+
+// Layer statistics, pass 1: the first n_hess workgroups are the h partial pass over X, the rest
+// the amax partial pass over W (both streaming, one launch).
+template <bool XBF16, int V, bool WBF16>
+__global__ __launch_bounds__(64 * V) void k_stats_partial(
+    const uint8_t* __restrict__ X, int64_t in, int64_t ldx_bytes, GroupMap map, int64_t n_strips,
+    double* __restrict__ partial, int64_t n_hess, const uint8_t* __restrict__ W, int64_t out,
+    AmaxPlan ap, int64_t ldw_bytes, uint32_t* __restrict__ amax_partial) {
+    __shared__ double red[V][XCols<XBF16>::kStrip];
+    if ((int64_t)blockIdx.x < n_hess) {
+        hess_partial_body<XBF16, V>(X, in, ldx_bytes, map, n_strips, partial, 0, blockIdx.x, red);
+    } else {
+        const int64_t blk = blockIdx.x - n_hess;
+        const uint32_t m = amax_chunk<WBF16, 64 * V>(W, out, ap.vpr, ldw_bytes, ap.chunk, blk,
+                                                     reinterpret_cast<uint32_t*>(&red[0][0]));
+        if (threadIdx.x == 0) amax_partial[blk] = m;
+    }
+}
+
+// Layer statistics, pass 2: the first n_fin workgroups finalize h, the last one computes S.
+__global__ __launch_bounds__(kFinThreads) void k_stats_finalize(
+    const double* __restrict__ partial, int64_t in, GroupMap map, double* __restrict__ h_acc,
+    float* __restrict__ h, int accumulate, int64_t n_fin, const uint32_t* __restrict__ amax_partial,
+    int64_t nblk, int rule, float* __restrict__ S) {
+    __shared__ double red[kFinSubs][kFinCols];
+    if ((int64_t)blockIdx.x < n_fin) {
+        hess_finalize_body(partial, in, map, h_acc, h, accumulate, blockIdx.x, 0, red);
+    } else {
+        const float s = scale_from_amax_partials<kFinThreads>(
+            amax_partial, nblk, rule, reinterpret_cast<uint32_t*>(&red[0][0]));
+        if (threadIdx.x == 0) S[0] = s;
     }
 }
 
@@ -313,6 +363,50 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
     const dim3 fgrid((uint32_t)((in + kFinCols - 1) / kFinCols), (uint32_t)E);
     hipLaunchKernelGGL(k_hess_finalize, fgrid, dim3(kFinThreads), 0, stream, partial, in, map,
                        h_acc, h, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+size_t layer_statistics_workspace_bytes(int64_t tokens, int64_t in, int64_t out) {
+    return round_up(hessian_workspace_bytes(tokens, in, 1)) +
+           (size_t)amax_plan(1, out, in, false).nblk * sizeof(uint32_t);
+}
+
+hipError_t launch_layer_statistics(const void* X, bool x_bf16, int64_t tokens, int64_t in,
+                                   int64_t ldx, double* h_acc, float* h, bool accumulate,
+                                   const void* W, bool w_bf16, int64_t out, int64_t ldw, int rule,
+                                   float* S, void* workspace, hipStream_t stream) {
+    GroupMap map{nullptr, nullptr, 1, tokens, rows_per_group(tokens, in, x_bf16)};
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    double* partial = reinterpret_cast<double*>(ws);
+    uint32_t* amax_partial =
+        reinterpret_cast<uint32_t*>(ws + round_up(hessian_workspace_bytes(tokens, in, 1)));
+    const AmaxPlan ap = amax_plan(1, out, in, w_bf16);
+    const int64_t n_strips = strips_for(in, x_bf16);
+    const int64_t n_hess = n_strips * max_groups(tokens, in, 1, x_bf16);
+    const int64_t ldx_bytes = ldx * (x_bf16 ? 2 : 4), ldw_bytes = ldw * (w_bf16 ? 2 : 4);
+    const uint8_t* Xb = static_cast<const uint8_t*>(X);
+    const uint8_t* Wb = static_cast<const uint8_t*>(W);
+    // the workgroup shape follows the h pass (the larger of the two streams)
+    const bool wide = tokens * in * (x_bf16 ? 2 : 4) >= kWideBytes;
+    const dim3 grid((uint32_t)(n_hess + ap.nblk));
+#define NVFP4_STATS(XB, V, WB)                                                                  \
+    hipLaunchKernelGGL((k_stats_partial<XB, V, WB>), grid, dim3(64 * V), 0, stream, Xb, in,     \
+                       ldx_bytes, map, n_strips, partial, n_hess, Wb, out, ap, ldw_bytes,       \
+                       amax_partial)
+    if (x_bf16 && wide) {
+        if (w_bf16) NVFP4_STATS(true, 4, true); else NVFP4_STATS(true, 4, false);
+    } else if (x_bf16) {
+        if (w_bf16) NVFP4_STATS(true, 8, true); else NVFP4_STATS(true, 8, false);
+    } else if (wide) {
+        if (w_bf16) NVFP4_STATS(false, 4, true); else NVFP4_STATS(false, 4, false);
+    } else {
+        if (w_bf16) NVFP4_STATS(false, 8, true); else NVFP4_STATS(false, 8, false);
+    }
+#undef NVFP4_STATS
+    const int64_t n_fin = (in + kFinCols - 1) / kFinCols;
+    hipLaunchKernelGGL(k_stats_finalize, dim3((uint32_t)(n_fin + 1)), dim3(kFinThreads), 0, stream,
+                       partial, in, map, h_acc, h, accumulate ? 1 : 0, n_fin, amax_partial,
+                       ap.nblk, rule, S);
     return hipGetLastError();
 }
 

@@ -42,6 +42,21 @@ hipError_t launch_amax_partial(const void* W, bool bf16, int64_t batch, int64_t 
                                int64_t ldw, int64_t stride_w, uint32_t* partial,
                                hipStream_t stream);
 
+// How the global-scale pass splits a matrix: nblk workgroups per matrix, each over `chunk`
+// 16-byte vectors (vpr per row).
+struct AmaxPlan {
+    int64_t nblk, chunk, vpr;
+};
+AmaxPlan amax_plan(int64_t batch, int64_t out, int64_t in, bool bf16);
+
+// Layer statistics: h of X and S of W (one matrix, one token chunk) in two launches, each
+// result bit-identical to launch_diag_hessian and launch_global_scale.
+size_t layer_statistics_workspace_bytes(int64_t tokens, int64_t in, int64_t out);
+hipError_t launch_layer_statistics(const void* X, bool x_bf16, int64_t tokens, int64_t in,
+                                   int64_t ldx, double* h_acc, float* h, bool accumulate,
+                                   const void* W, bool w_bf16, int64_t out, int64_t ldw, int rule,
+                                   float* S, void* workspace, hipStream_t stream);
+
 // Where the search takes S from: S[batch] as given, or (one matrix) reduced in every
 // workgroup from the amax partials with the rule, workgroup 0 also writing it to S_out.
 struct ScaleSource {

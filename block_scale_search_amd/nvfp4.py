@@ -38,6 +38,9 @@ _SIGS = {
     "nvfp4_diag_hessian_batched": ([_P, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_global_scale_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_global_scale": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
+    "nvfp4_layer_statistics_workspace_size": ([_I64, _I64, _I64], _SZ),
+    "nvfp4_layer_statistics": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _P, _I, _I64, _I64, _I, _P,
+                                _P, _SZ, _P], _I),
     "nvfp4_scale_search": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I, _I32, _I32, _I,
                             _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
@@ -130,6 +133,10 @@ def nvfp4_global_scale_workspace_size(batch: int, out: int, inp: int) -> int:
     return int(_lib.nvfp4_global_scale_workspace_size(batch, out, inp))
 
 
+def nvfp4_layer_statistics_workspace_size(tokens: int, inp: int, out: int) -> int:
+    return int(_lib.nvfp4_layer_statistics_workspace_size(tokens, inp, out))
+
+
 def nvfp4_diag_hessian(X, tokens, inp, ldx, h_acc, h, accumulate, workspace, stream=None, prepare=False):
     """h_acc = h = None: deferred mode (row-group sums into the workspace only)."""
     if h_acc is not None:
@@ -171,6 +178,20 @@ def nvfp4_global_scale(W, batch, out, inp, ldw, stride_w, rule, S, workspace, st
     return _run("nvfp4_global_scale", (
         _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
         rule, _dev(S, "S", (torch.float32,)), _dev(workspace, "workspace"),
+        workspace.numel() * workspace.element_size(), _stream(stream)), prepare)
+
+
+def nvfp4_layer_statistics(X, tokens, inp, ldx, h_acc, h, accumulate, W, out, ldw, rule, S,
+                           workspace, stream=None, prepare=False):
+    _need(h_acc, inp, "h_acc")
+    if h is not None:
+        _need(h, inp, "h")
+    _need(S, 1, "S")
+    return _run("nvfp4_layer_statistics", (
+        _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx,
+        _dev(h_acc, "h_acc", (torch.float64,)), _dev(h, "h", (torch.float32,)), int(accumulate),
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), out, ldw, rule,
+        _dev(S, "S", (torch.float32,)), _dev(workspace, "workspace"),
         workspace.numel() * workspace.element_size(), _stream(stream)), prepare)
 
 
@@ -319,6 +340,24 @@ def diag_hessian_batched(X: torch.Tensor, seg_offsets: torch.Tensor,
     nvfp4_diag_hessian_batched(X, seg_offsets, E, T, n, X.stride(0), h_acc, h, accumulate, ws,
                                stream)
     return h_acc, h
+
+
+def layer_statistics(X: torch.Tensor, W: torch.Tensor, rule: int = GS_AMAX_448,
+                     h_acc: torch.Tensor | None = None, accumulate: bool = False, stream=None):
+    """h over X [tokens, in] and S of W [out, in]; returns (h_acc f64 [in], h f32 [in], S [1])."""
+    T, n = X.shape
+    o = W.shape[0]
+    if X.stride(1) != 1 or W.stride(1) != 1:
+        raise ValueError("X and W rows must be contiguous")
+    if h_acc is None:
+        h_acc = torch.zeros(n, dtype=torch.float64, device=X.device)
+    h = torch.empty(n, dtype=torch.float32, device=X.device)
+    S = torch.empty(1, dtype=torch.float32, device=X.device)
+    ws = torch.empty(max(16, nvfp4_layer_statistics_workspace_size(T, n, o)), dtype=torch.uint8,
+                     device=X.device)
+    nvfp4_layer_statistics(X, T, n, X.stride(0), h_acc, h, accumulate, W, o, W.stride(0), rule, S,
+                           ws, stream)
+    return h_acc, h, S
 
 
 def global_scale(W: torch.Tensor, rule: int = GS_AMAX_448, stream=None) -> torch.Tensor:

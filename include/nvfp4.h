@@ -130,6 +130,32 @@ nvfp4_status nvfp4_global_scale(const void* W, int w_dtype, int64_t batch, int64
                                 void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Steps 1 and 2 together for one layer: h of its calibration activations X and the global scale
+ * S of its weight matrix W ([HS] §3 / App. B: h = diag(X^T X) and the tensor-level FP32 scale
+ * are the two per-layer inputs of the search; [SS] §2: the 256 * 6 rule).
+ *
+ * Results are bit-identical to nvfp4_diag_hessian(X, ..., h_acc, h, accumulate) followed by
+ * nvfp4_global_scale(W, 1 matrix, ..., rule, S); the two reductions share two launches instead
+ * of four, which shortens a layer's chain of dependent launches.
+ *
+ * X, tokens, in, ldx, h_acc, h, accumulate  as for nvfp4_diag_hessian (one token chunk, h_acc
+ *          required).
+ * W        device, bf16 or f32 [out, in], row stride ldw, 16-byte aligned rows (the layer's
+ *          weights: their `in` is X's).
+ * rule     NVFP4_GS_AMAX_448 or NVFP4_GS_AMAX_256; S device float [1].
+ * workspace  device, nvfp4_layer_statistics_workspace_size(tokens, in, out) bytes, 16-byte
+ *          aligned; overwritten, no initialisation needed.
+ * Argument errors are those of the two calls it replaces.
+ * ------------------------------------------------------------------------------------------- */
+size_t nvfp4_layer_statistics_workspace_size(int64_t tokens, int64_t in, int64_t out);
+
+nvfp4_status nvfp4_layer_statistics(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                    int64_t ldx, double* h_acc, float* h, int accumulate,
+                                    const void* W, int w_dtype, int64_t out, int64_t ldw, int rule,
+                                    float* S, void* workspace, size_t workspace_bytes,
+                                    void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Steps 3-4: per-group E4M3 scale search, fused with quantize + pack.
  *
  * For group g of 16 consecutive input columns of row o of matrix b ([HS] §3 and [SR] §4.1.1:

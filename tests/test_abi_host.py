@@ -237,3 +237,31 @@ def test_diag_hessian_rejects_bad_arguments(lib):
     assert B(FAKE, 1, None, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, wsb, None) == n.ERR_NULL
     assert B(FAKE, 1, FAKE, 0, 1000, 64, 64, FAKE, FAKE, 0, FAKE, wsb, None) == n.ERR_SHAPE
     assert B(FAKE, 1, FAKE, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_WORKSPACE
+
+
+def test_layer_statistics_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    ws = lib.nvfp4_layer_statistics_workspace_size(1000, 64, 4)
+    assert ws >= lib.nvfp4_diag_hessian_workspace_size(1000, 64, 1)   # h partials + amax partials
+    assert lib.nvfp4_layer_statistics_workspace_size(-1, 64, 4) == 0
+
+    def call(**kw):
+        a = dict(X=FAKE, xd=1, T=1000, inp=64, ldx=64, acc=FAKE, h=FAKE, accum=0, W=FAKE, wd=1,
+                 out=4, ldw=64, rule=0, S=FAKE, ws=FAKE, wsb=ws)
+        a.update(kw)
+        return lib.nvfp4_layer_statistics(a["X"], a["xd"], a["T"], a["inp"], a["ldx"], a["acc"],
+                                          a["h"], a["accum"], a["W"], a["wd"], a["out"], a["ldw"],
+                                          a["rule"], a["S"], a["ws"], a["wsb"], None)
+    assert call(xd=4) == n.ERR_DTYPE
+    assert call(wd=4) == n.ERR_DTYPE
+    assert call(inp=40, ldx=40, ldw=40) == n.ERR_SHAPE                    # W's in % 16
+    assert call(ldx=60) == n.ERR_SHAPE
+    assert call(rule=2) == n.ERR_ARG
+    assert call(acc=None) == n.ERR_NULL
+    assert call(S=None) == n.ERR_NULL
+    assert call(W=None) == n.ERR_NULL
+    assert call(X=ODD) == n.ERR_ALIGN
+    assert call(W=ODD) == n.ERR_ALIGN
+    assert call(wsb=ws - 1) == n.ERR_WORKSPACE
+    assert call(ws=None) == n.ERR_WORKSPACE
+    assert call(inp=0, ldx=0, ldw=0, X=None, acc=None, W=None, S=None, ws=None, wsb=0) == n.OK
