@@ -217,6 +217,28 @@ def algorithmic(cfg, label: str):
     return bytes_, flops
 
 
+def cpu_time(fn, min_s: float = 2.0):
+    """Wall seconds per call of fn (repeated until min_s has passed)."""
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return el / n
+
+
+def host_array(t):
+    """A device tensor as the oracle takes it (bf16 as uint16 bit patterns)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
 def cpu_baseline(cfg, layer, threads: int):
     """The oracle, as it stands, on a bounded sample of the first input set (the GPU's own
     inputs, copied to the host), projected to the whole step.
@@ -464,6 +486,19 @@ def main():
               "note": "E = W - W_hat runs as bf16 E_hi + E_lo, so the MFMAs issue twice the "
                       "algorithmic flops; the time includes the residual split and the "
                       "reduction kernels"}
+        if not args.no_cpu:
+            import oracle
+            Ts = min(T0, 512)
+            s_ = runner.sets[0]
+            Xh, Wh = host_array(s_.chunks[0][:Ts]), host_array(s_.W)
+            ph = host_array(s_.packed[-1]).reshape(cfg.out, cfg.inp // 2)
+            sh = host_array(s_.scales[-1]).reshape(cfg.out, cfg.inp // 16)
+            Sh = float(s_.S.item())
+            t_cpu = cpu_time(lambda: oracle.output_error(Xh, Wh, ph, sh, Sh))
+            oe["cpu_oracle"] = {"kind": "oracle", "us_projected": round(t_cpu * 1e6 * T0 / Ts, 1),
+                                "sample": f"{Ts} of {T0} tokens, projected by the token ratio",
+                                "cores": len(os.sched_getaffinity(0)),
+                                "note": "binary64 numpy (its matmul uses the BLAS threads)"}
 
     # on-line activation quantisation (outside the step): one kernel pair vs global scale +
     # search (three kernels), on a prefill chunk and a decode batch
@@ -506,6 +541,16 @@ def main():
                           "us_global_scale_then_search": round(us2, 2),
                           "GB/s": round(nbytes / us1 / 1e3, 1),
                           "weights/s": Ta * na / (us1 * 1e-6)}
+            if not args.no_cpu and Ta <= 1024:
+                import oracle
+                Xh = host_array(Xa)
+                thr = min(16, len(os.sched_getaffinity(0)))
+
+                def cpu_act():
+                    So = oracle.global_scale(Xh, oracle.GS_AMAX_256)
+                    oracle.scale_search(Xh, None, oracle.MSE, -3, 7, False, So, threads=thr)
+                acts[name]["cpu_oracle_us"] = round(cpu_time(cpu_act, 1.0) * 1e6, 1)
+                acts[name]["cpu_oracle_threads"] = thr
 
     # GPTQ (outside the step): the damped inverse-Hessian factor is caller-side preparation
     # (binary64 Gram matrix, inverse and Cholesky), untimed; the library call is timed
@@ -544,6 +589,19 @@ def main():
               "TOP/s": round((n_fma + search_ops) / g_us / 1e6, 2),
               "frac_valu_issue": round((n_fma + search_ops) / g_us / 1e6 / VALU_PEAK_TOPS, 4),
               "weights/s": cfg.out * cfg.inp / (g_us * 1e-6)}
+        if not args.no_cpu:
+            import oracle
+            rows = min(cfg.out, 128)
+            Wh = host_array(s0.W[:rows])
+            Uh, hh = U.cpu().numpy(), hd.cpu().numpy()
+            Sh = float(s0.S.item())
+            thr = min(16, len(os.sched_getaffinity(0)))
+            t_cpu = cpu_time(lambda: oracle.gptq(Wh, Uh, hh, oracle.WMSE, m.lo, m.hi, Sh,
+                                                 threads=thr))
+            gq["cpu_oracle"] = {"kind": "oracle", "ms_projected": round(t_cpu * 1e3 * cfg.out / rows, 1),
+                                "sample": f"{rows} of {cfg.out} rows (rows are independent), "
+                                          "projected by the row ratio",
+                                "cores": thr}
 
     per_label = {}
     for row in ev:
