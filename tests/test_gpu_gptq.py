@@ -6,7 +6,8 @@ Cases: inner blocks of 64 columns with a ragged last block (in = 208), several o
 256 with a ragged last one (in = 592: 256 + 256 + 64 + 16), rows off the 16-row and 128-row
 tiles, bf16 and f32 W, WMSE and MSE windows, a wide window clipped at codes 1 and 126 (scored
 16 codes per pass), a one-code window, all-zero groups and negative zeros, the identity factor
-(no propagation), and a Hessian from correlated activations (strong propagation)."""
+(no propagation), a Hessian from correlated activations (strong propagation), and the full
+8B-shaped layers (4096 x 4096 and 4096 x 14336) checked on sampled rows."""
 import numpy as np
 import pytest
 import torch
@@ -92,3 +93,39 @@ def test_gptq_zero_groups_and_negative_zeros(nv):
     W[9, 256:272] = 0.0
     _compare(nv, W, U, h, "wmse", -9, 6)
     _compare(nv, W, U, h, "mse", -3, 7)
+
+
+def _workload_factor(cfg, W):
+    """U and h of a workload's first activation chunk, as bench.py builds them (binary64 Gram
+    matrix on the GPU, damping 0.01 mean(diag), Cholesky factor of the inverse)."""
+    sig = workloads.make_sigma(cfg, DEV)
+    X, _ = workloads.make_activation_chunk(cfg, sig, 0, DEV)
+    Xd = X.double()
+    H = Xd.T @ Xd
+    del Xd, X
+    H += 0.01 * torch.diagonal(H).mean() * torch.eye(cfg.inp, dtype=torch.float64, device=DEV)
+    U = torch.linalg.cholesky(torch.cholesky_inverse(torch.linalg.cholesky(H))).T.contiguous()
+    return U.float().contiguous(), torch.diagonal(H).float().contiguous()
+
+
+@pytest.mark.parametrize("name,lo,hi", [("attn8b", -8, 7), ("down8b", -9, 6)])
+def test_gptq_full_size_sampled_rows(nv, name, lo, hi):
+    """Full 8B-shaped layers on the GPU; rows are independent, so sampled rows (first, last and
+    seeded ones) are checked bit-exact against the oracle run on those rows alone."""
+    cfg = workloads.CONFIGS[name]
+    W = workloads.make_weights(cfg, DEV)
+    U, h = _workload_factor(cfg, W)
+    S = nv.global_scale(W, nv.GS_AMAX_256 if cfg.gs_rule == "amax256" else nv.GS_AMAX_448)
+    g = nv.gptq(W, U, h, S, nv.WMSE, lo, hi, with_final=True)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, cfg.out - 1], rng.choice(cfg.out, 29, replace=False)]))
+    o = oracle.gptq(host_w(W[torch.from_numpy(rows).to(DEV)]), U.cpu().numpy(), h.cpu().numpy(),
+                    oracle.WMSE, lo, hi, float(S.item()))
+    for k in ("scales", "packed"):
+        got = g[k][torch.from_numpy(rows).to(DEV)].cpu().numpy()
+        bad = np.argwhere(got != o[k])
+        assert bad.size == 0, f"{name} {k}: {len(bad)} mismatches, first {bad[:3].tolist()}"
+    wf = g["W_final"][torch.from_numpy(rows).to(DEV)].cpu().numpy()
+    bad = np.argwhere(wf.view(np.uint32) != o["W_final"].view(np.uint32))
+    assert bad.size == 0, f"{name} W_final: {len(bad)} mismatches, first {bad[:3].tolist()}"
