@@ -288,27 +288,42 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
     const int n = hi - lo + 1;
     uint8_t* scale_row = scales + (s.valid ? r : 0) * (in / 16) + o0 / 16;
 
+    // U staging of an inner block: thread tid holds the 16 float4 of rows J = tid / 64 + 4q,
+    // slot (tid / 16) % 4, lane tid % 16 (q = 0..15). The next inner block's are loaded into
+    // registers before this block's columns run, so their latency overlaps the column chain.
+    float4 pre[16];
+    const int sl_t = (tid >> 4) & 3, tt_t = tid & 15, k_t = 64 * sl_t + 4 * tt_t;
+    auto load_u = [&](int ib) {
+        const int64_t b0 = o0 + (int64_t)ib * kB;
+        const int bc = min(kB, oc - ib * kB), rest = oc - ib * kB;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int J = (tid >> 6) + 4 * q;
+            pre[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (J < bc && k_t < rest)
+                pre[q] = *reinterpret_cast<const float4*>(U + (b0 + J) * in + b0 + k_t);
+        }
+    };
+    load_u(0);
     for (int ib = 0; ib * kB < oc; ++ib) {
         const int64_t b0 = o0 + (int64_t)ib * kB;       // first column of the inner block
         const int bc = min(kB, oc - ib * kB);
-        const int rest = oc - ib * kB;                  // columns from b0 to the outer end
         __syncthreads();                                // the previous inner block's readers
-        for (int i = tid; i < kB * 4 * 16; i += 256) {
-            const int J = i >> 6, sl = (i >> 4) & 3, tt = i & 15;
-            const int k = 64 * sl + 4 * tt;             // column offset from b0
-            float4 v = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (J < bc && k < rest)
-                v = *reinterpret_cast<const float4*>(U + (b0 + J) * in + b0 + k);
-            if (sl == 0) {
-                if (J >= k && J < k + 4) L.ud[J] = J < bc ? (&v.x)[J - k] : 1.0f;
-                v.x = k + 0 > J ? v.x : 0.0f;
-                v.y = k + 1 > J ? v.y : 0.0f;
-                v.z = k + 2 > J ? v.z : 0.0f;
-                v.w = k + 3 > J ? v.w : 0.0f;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+            const int J = (tid >> 6) + 4 * q;
+            float4 v = pre[q];
+            if (sl_t == 0) {
+                if (J >= k_t && J < k_t + 4) L.ud[J] = J < bc ? (&v.x)[J - k_t] : 1.0f;
+                v.x = k_t + 0 > J ? v.x : 0.0f;
+                v.y = k_t + 1 > J ? v.y : 0.0f;
+                v.z = k_t + 2 > J ? v.z : 0.0f;
+                v.w = k_t + 3 > J ? v.w : 0.0f;
             }
-            L.us[J][sl][tt] = v;
+            L.us[J][sl_t][tt_t] = v;
         }
         __syncthreads();
+        if ((ib + 1) * kB < oc) load_u(ib + 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) s.dg[e] = L.ud[4 * t + e];
         s.nib = 0u;
