@@ -101,15 +101,13 @@ constexpr int kBlockRows = 16;  // rows per block-kernel workgroup (256 threads)
 struct OuterLane {
     float w[16];       // current values
     float dg[4];       // slot 0: U[c][c] of the lane's 4 columns
-    uint32_t nib;      // E2M1 code of the previous (even) column
+    float wq[4];       // slot 0: each column's value when it was quantised
+    float ev[4];       // slot 0: each column's error
+    uint32_t nibs;     // slot 0: the 4 columns' E2M1 codes, column 4t + e at bit 4e
     float2 er;         // (eff, r) of the current group's code
     float4 u[4];       // the lane's U entries of the current column, one float4 per slot
     int t;             // lane within the row
     bool valid;
-    float* wrow;       // the row's final values at the inner block's first column
-    float* ecol;       // the row's error of the current column (column stride ldE)
-    int64_t ldE;
-    uint8_t* prow;     // the row's code bytes at the inner block's first column
 };
 
 // LDS of the outer-block kernel. us[J][s][t] holds U[row J of the inner block][the 4 columns of
@@ -201,15 +199,13 @@ __device__ __forceinline__ void outer_step(OuterLane& s, const OuterLds& L, int 
     const float v = q * s.er.x;
     const float err_own = __fdiv_rn(wj - v, s.dg[e]);
     const float err = row_bcast<(J >> 2)>(err_own);
-    // the lane holding column J stores its final value, its error and (at odd J) the code byte
-    // of columns J - 1 and J, even column in the low nibble
-    if (s.valid && s.t == (J >> 2) && J < bc) {
-        s.wrow[J] = wj;
-        *s.ecol = err_own;
-        if constexpr ((J & 1) == 1) s.prow[J / 2] = (uint8_t)(s.nib | ((byte & 15u) << 4));
-    }
-    if constexpr ((J & 1) == 0) s.nib = byte & 15u;
-    s.ecol += s.ldE;
+    // the lane holding column J keeps its value, error and code (selects, no branch); they are
+    // stored after the inner block
+    const bool mine = s.t == (J >> 2);
+    s.wq[e] = mine ? wj : s.wq[e];
+    s.ev[e] = mine ? err_own : s.ev[e];
+    s.nibs = mine ? (s.nibs | ((byte & 15u) << (4 * e))) : s.nibs;
+    asm volatile("" : "+v"(s.wq[e]), "+v"(s.ev[e]), "+v"(s.nibs));
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
         const float4 u4 = s.u[sl];
@@ -325,17 +321,24 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
         __syncthreads();
         if ((ib + 1) * kB < oc) load_u(ib + 1);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) s.dg[e] = L.ud[4 * t + e];
-        s.nib = 0u;
-        const int64_t rr = s.valid ? r : 0;
-        s.wrow = Wf + rr * in + b0;
-        s.ecol = E + (int64_t)ib * kB * ldE + rr;
-        s.ldE = ldE;
-        s.prow = packed + rr * (in / 2) + b0 / 2;
+        for (int e = 0; e < 4; ++e) {
+            s.dg[e] = L.ud[4 * t + e];
+            s.wq[e] = s.ev[e] = 0.0f;
+        }
+        s.nibs = 0u;
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) s.u[sl] = L.us[0][sl][t];
         outer_steps<WMSE, NWIN>(s, L, bc, ib * kB, S, lo, n, scale_row + ib * (kB / 16),
                                 std::make_integer_sequence<int, kB>{});
+        if (s.valid && 4 * t < bc) {
+            *reinterpret_cast<float4*>(Wf + r * in + b0 + 4 * t) =
+                make_float4(s.wq[0], s.wq[1], s.wq[2], s.wq[3]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) E[(int64_t)(ib * kB + 4 * t + e) * ldE + r] = s.ev[e];
+            // columns 4t .. 4t + 3: two bytes, even column in the low nibble
+            *reinterpret_cast<uint16_t*>(packed + r * (in / 2) + (b0 + 4 * t) / 2) =
+                (uint16_t)s.nibs;
+        }
         // the next inner block's columns move to slot 0
 #pragma unroll
         for (int k = 0; k < 12; ++k) s.w[k] = s.w[k + 4];
