@@ -92,6 +92,17 @@ __device__ __forceinline__ int row_argmin(float L, int c) {
     return c;
 }
 
+// Workgroup barrier for LDS reuse only: waits for this wave's LDS accesses (lgkmcnt(0); the
+// vmcnt and expcnt fields at their maxima) and not for its global stores, which drain in the
+// background (nothing in the kernel reads them back). __syncthreads would also wait for the
+// previous inner block's stores, several microseconds per block.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 constexpr int kOB = 256;        // columns per outer block
 constexpr int kBlockRows = 16;  // rows per block-kernel workgroup (256 threads)
 
@@ -300,17 +311,32 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
                 pre[q] = *reinterpret_cast<const float4*>(U + (b0 + J) * in + b0 + k_t);
         }
     };
+    // results of an inner block, kept until they are stored
+    float pq[4], pe[4];
+    uint32_t pn = 0u;
+    auto store_block = [&](int ib) {
+        const int bc = min(kB, oc - ib * kB);
+        if (!s.valid || 4 * t >= bc) return;
+        const int64_t b0 = o0 + (int64_t)ib * kB;
+        *reinterpret_cast<float4*>(Wf + r * in + b0 + 4 * t) = make_float4(pq[0], pq[1], pq[2], pq[3]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) E[(int64_t)(ib * kB + 4 * t + e) * ldE + r] = pe[e];
+        // columns 4t .. 4t + 3: two bytes, even column in the low nibble
+        *reinterpret_cast<uint16_t*>(packed + r * (in / 2) + (b0 + 4 * t) / 2) = (uint16_t)pn;
+    };
     load_u(0);
     for (int ib = 0; ib * kB < oc; ++ib) {
         const int64_t b0 = o0 + (int64_t)ib * kB;       // first column of the inner block
         const int bc = min(kB, oc - ib * kB);
-        __syncthreads();                                // the previous inner block's readers
+        lds_barrier();                                  // the previous inner block's readers
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int J = (tid >> 6) + 4 * q;
             float4 v = pre[q];
             if (sl_t == 0) {
-                if (J >= k_t && J < k_t + 4) L.ud[J] = J < bc ? (&v.x)[J - k_t] : 1.0f;
+                const int dj = J - k_t;
+                const float dv = dj == 0 ? v.x : (dj == 1 ? v.y : (dj == 2 ? v.z : v.w));
+                if (dj >= 0 && dj < 4) L.ud[J] = J < bc ? dv : 1.0f;
                 v.x = k_t + 0 > J ? v.x : 0.0f;
                 v.y = k_t + 1 > J ? v.y : 0.0f;
                 v.z = k_t + 2 > J ? v.z : 0.0f;
@@ -318,7 +344,10 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
             }
             L.us[J][sl_t][tt_t] = v;
         }
-        __syncthreads();
+        lds_barrier();
+        // the previous inner block's results, stored only now: a store still in flight at the
+        // staging above would have been waited for with the prefetched loads
+        if (ib > 0) store_block(ib - 1);
         if ((ib + 1) * kB < oc) load_u(ib + 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -330,19 +359,17 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
         for (int sl = 0; sl < 4; ++sl) s.u[sl] = L.us[0][sl][t];
         outer_steps<WMSE, NWIN>(s, L, bc, ib * kB, S, lo, n, scale_row + ib * (kB / 16),
                                 std::make_integer_sequence<int, kB>{});
-        if (s.valid && 4 * t < bc) {
-            *reinterpret_cast<float4*>(Wf + r * in + b0 + 4 * t) =
-                make_float4(s.wq[0], s.wq[1], s.wq[2], s.wq[3]);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) E[(int64_t)(ib * kB + 4 * t + e) * ldE + r] = s.ev[e];
-            // columns 4t .. 4t + 3: two bytes, even column in the low nibble
-            *reinterpret_cast<uint16_t*>(packed + r * (in / 2) + (b0 + 4 * t) / 2) =
-                (uint16_t)s.nibs;
+        for (int e = 0; e < 4; ++e) {
+            pq[e] = s.wq[e];
+            pe[e] = s.ev[e];
         }
+        pn = s.nibs;
         // the next inner block's columns move to slot 0
 #pragma unroll
         for (int k = 0; k < 12; ++k) s.w[k] = s.w[k + 4];
     }
+    store_block((oc - 1) / kB);
 }
 
 template <bool WMSE, int NWIN>
