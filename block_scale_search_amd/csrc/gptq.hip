@@ -444,29 +444,43 @@ __device__ __forceinline__ void update_body(UpdateLds& L, uint32_t bx, uint32_t 
             acc[a][4 * hb + 3] = v.w;
         }
     }
+    constexpr int QE = kUc * RT / 4 / 256, QU = kUc * 128 / 4 / 256;
+    float4 pe[QE], pu[QU];
+    auto load_chunk = [&](int jc) {
+        const int m = min(kUc, nj - jc);
+#pragma unroll
+        for (int q = 0; q < QE; ++q) {
+            const int i = tid + 256 * q;
+            const int jj = i / (RT / 4), x4 = (i % (RT / 4)) * 4;
+            pe[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (jj < m && r0 + x4 < out)   // rows out .. ldE - 1 are padding
+                pe[q] = *reinterpret_cast<const float4*>(E + (jc + jj) * ldE + r0 + x4);
+        }
+#pragma unroll
+        for (int q = 0; q < QU; ++q) {
+            const int i = tid + 256 * q;
+            const int jj = i >> 5, x4 = (i & 31) * 4;
+            pu[q] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            if (jj < m && c0 + x4 < k1)
+                pu[q] = *reinterpret_cast<const float4*>(U + (j0 + jc + jj) * in + c0 + x4);
+        }
+    };
+    load_chunk(0);
     for (int jc = 0; jc < nj; jc += kUc) {
         const int m = min(kUc, nj - jc);
         __syncthreads();
-        // kUc x RT errors and kUc x 128 U entries
 #pragma unroll
-        for (int q = 0; q < kUc * RT / 4 / 256; ++q) {
+        for (int q = 0; q < QE; ++q) {
             const int i = tid + 256 * q;
-            const int jj = i / (RT / 4), x4 = (i % (RT / 4)) * 4;
-            float4 ve = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (jj < m && r0 + x4 < out)   // rows out .. ldE - 1 are padding
-                ve = *reinterpret_cast<const float4*>(E + (jc + jj) * ldE + r0 + x4);
-            *reinterpret_cast<float4*>(&es[jj][x4]) = ve;
+            *reinterpret_cast<float4*>(&es[i / (RT / 4)][(i % (RT / 4)) * 4]) = pe[q];
         }
 #pragma unroll
-        for (int q = 0; q < kUc * 128 / 4 / 256; ++q) {
+        for (int q = 0; q < QU; ++q) {
             const int i = tid + 256 * q;
-            const int jj = i >> 5, x4 = (i & 31) * 4;
-            float4 vu = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (jj < m && c0 + x4 < k1)
-                vu = *reinterpret_cast<const float4*>(U + (j0 + jc + jj) * in + c0 + x4);
-            *reinterpret_cast<float4*>(&us[jj][x4]) = vu;
+            *reinterpret_cast<float4*>(&us[i >> 5][(i & 31) * 4]) = pu[q];
         }
         __syncthreads();
+        if (jc + kUc < nj) load_chunk(jc + kUc);
         for (int jj = 0; jj < m; ++jj) {
             float e[TR];
             if constexpr (TR == 8) {
