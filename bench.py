@@ -54,6 +54,7 @@ FLOPS_PER_ELEM_CAND = {"wmse": 7, "mse": 6}
 METRIC = "weights/s and HBM GB/s (fraction of peak) for scale search+pack; h-reduce GB/s"
 KERNEL_SOURCES = ["block_scale_search_amd/csrc/scale_search.hip",
                   "block_scale_search_amd/csrc/search_device.h",
+                  "block_scale_search_amd/csrc/amax_device.h",
                   "block_scale_search_amd/csrc/device_formats.h"]
 
 

@@ -2,6 +2,7 @@
 // search_device.h).
 #include <hip/hip_runtime.h>
 
+#include "amax_device.h"
 #include "device_formats.h"
 #include "internal.h"
 #include "search_device.h"
@@ -32,23 +33,6 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, float 
             w[4 * i + 3] = v.w;
         }
     }
-}
-
-// S of one matrix from its amax partials (bit patterns of non-negative binary32 values), by the
-// same formula as the global-scale kernel: amax / 2688 or amax / 1536, 1 for amax = 0.
-__device__ __forceinline__ float scale_from_partials(const uint32_t* __restrict__ partial,
-                                                     int64_t n, int rule, uint32_t* wmax) {
-    uint32_t m = 0u;
-    for (int64_t i = threadIdx.x; i < n; i += kSearchThreads) m = max(m, partial[i]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, off, 64));
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
-    __syncthreads();
-    uint32_t r = wmax[0];
-#pragma unroll
-    for (int i = 1; i < kSearchThreads / 64; ++i) r = max(r, wmax[i]);
-    const float amax = __uint_as_float(r);
-    return amax > 0.0f ? __fdiv_rn(amax, rule == 0 ? 2688.0f : 1536.0f) : 1.0f;
 }
 
 // PROPOSAL: the window is centred on a per-group proposal code center[] instead of the base
@@ -101,7 +85,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
 
     float S;
     if constexpr (SFP) {
-        S = scale_from_partials(src.amax_partial, src.n_partial, src.rule, wmax);
+        S = scale_from_amax_partials<kSearchThreads>(src.amax_partial, src.n_partial, src.rule,
+                                                     wmax);
         if (blockIdx.x == 0 && threadIdx.x == 0 && src.S_out) src.S_out[0] = S;
     } else {
         S = src.S[batch];

@@ -303,15 +303,10 @@ __device__ __forceinline__ bool build_table(float S, float2* tab, int* flag) {
 
 // Base code of a group: E4M3 round-to-nearest-even of (absmax / 6) / S, at least 1; 0 for an
 // all-zero group.
-// The maximum is taken as a tree (4 dependent steps instead of 16); fmaxf ignores a NaN operand,
-// so the result is the largest non-NaN |w| in any order, and NaN only when all 16 are NaN.
 __device__ __forceinline__ int base_code(const float (&w)[16], float S) {
-    float m[8];
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m[i] = fmaxf(fabsf(w[2 * i]), fabsf(w[2 * i + 1]));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m[i] = fmaxf(m[2 * i], m[2 * i + 1]);
-    const float amax = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+    for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(w[j]));
     if (!(amax > 0.0f)) return 0;
     const float s_star = __fdiv_rn(__fdiv_rn(amax, 6.0f), S);
     return max(e4m3_rne_sat(s_star), 1);
