@@ -457,6 +457,25 @@ def main():
     torch.cuda.synchronize()
     pack_us = p0.elapsed_time(p1) * 1e3 / reps
 
+    # the h-reduce alone (nvfp4_diag_hessian on each set's X), outside the step, where the step
+    # runs it fused with the global scale
+    h_alone_us = None
+    if any(s_.seg is None and len(s_.chunks) == 1 for s_ in runner.sets[:1]) and \
+            not runner.separate_stats:
+        hs_ = [nv.nvfp4_diag_hessian(s_.chunks[0], s_.chunks[0].shape[0], cfg.inp, cfg.inp,
+                                     s_.h_acc, s_.h, False, runner.ws_h, prepare=True)
+               for s_ in runner.sets]
+        for f in hs_:
+            f()
+        torch.cuda.synchronize()
+        reps_h = 20 * n_sets
+        p0.record(main)
+        for i in range(reps_h):
+            hs_[i % n_sets]()
+        p1.record(main)
+        torch.cuda.synchronize()
+        h_alone_us = p0.elapsed_time(p1) * 1e3 / reps_h
+
     # layer-output error (evaluation, outside the step): X chunk 0 against W and the last
     # mode's codes of each input set
     oe = None
@@ -629,6 +648,12 @@ def main():
         kernels[lab] = k
     wb = 2 if str(cfg.w_dtype).endswith("bfloat16") else 4
     pack_bytes = cfg.n_weights * wb + cfg.n_weights // 2 + cfg.n_weights // 16
+    if h_alone_us is not None:
+        xb = (cfg.chunk_tokens or cfg.tokens) * cfg.inp * 2
+        kernels["h_reduce alone (outside the step)"] = {
+            "avg_us": round(h_alone_us, 3), "x_bytes": xb,
+            "GB/s": round(xb / h_alone_us / 1e3, 1),
+            "frac_hbm": round(xb / h_alone_us / 1e3 / HBM_PEAK_GBS, 4)}
     kernels["pack (outside the step)"] = {
         "avg_us": round(pack_us, 3), "calls_per_step": 0, "alg_bytes": pack_bytes,
         "GB/s": round(pack_bytes / pack_us / 1e3, 1),
@@ -699,6 +724,8 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "h_reduce_GB/s" if "h_reduce" in kernels else "h_and_global_scale_GB/s": h_stage_gbs,
+        **({"h_reduce_alone_GB/s": kernels["h_reduce alone (outside the step)"]["GB/s"]}
+           if "h_reduce alone (outside the step)" in kernels else {}),
     }
     if oe is not None:
         line["output_error"] = oe
