@@ -337,6 +337,7 @@ nvfp4_status nvfp4_gptq(const void* W, int w_dtype, int64_t out, int64_t in, int
     nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
     if (st != NVFP4_OK) return st;
     if (out * in >= ((int64_t)1 << 39)) return NVFP4_ERR_SHAPE;
+    if ((out + 31) / 32 > 65535) return NVFP4_ERR_SHAPE;   // row tiles of the update grid
     if (out == 0 || in == 0) return NVFP4_OK;
     const bool wmse = objective == NVFP4_WMSE;
     if (U == nullptr || S == nullptr || scales == nullptr || packed == nullptr ||

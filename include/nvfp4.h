@@ -252,7 +252,10 @@ nvfp4_status nvfp4_pack(const void* W, int w_dtype, int64_t batch, int64_t out, 
  * W         device, bf16 or f32 [out, in], row stride ldw (16-byte aligned rows).
  * U         device float [in, in] row-major, 16-byte aligned: the upper-triangular factor of the
  *           damped inverse Hessian, (H + damping)^-1 = U^T U (entries below the diagonal are not
- *           read); computed by the caller, e.g. with a Cholesky routine.
+ *           read); computed by the caller, e.g. with a Cholesky routine. Its diagonal must be
+ *           positive and finite (as a Cholesky factor's is); otherwise the propagated values are
+ *           not finite and the outputs are unspecified.
+ * Shapes: in % 16 == 0, out * in < 2^39 and out <= 2,097,120 (else NVFP4_ERR_SHAPE).
  * h         device float [in], the diagonal weights of the search (WMSE), e.g. diag(H); NULL
  *           for MSE.
  * S         device float [1]: the global scale (e.g. from nvfp4_global_scale on W).
