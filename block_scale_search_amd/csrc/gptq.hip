@@ -326,7 +326,6 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
     };
     load_u(0);
     for (int ib = 0; ib * kB < oc; ++ib) {
-        const int64_t b0 = o0 + (int64_t)ib * kB;       // first column of the inner block
         const int bc = min(kB, oc - ib * kB);
         lds_barrier();                                  // the previous inner block's readers
 #pragma unroll
