@@ -7,8 +7,9 @@ raises ``Nvfp4Error`` on a non-OK status. Every computation runs in the library'
 there is no CPU path. Importing this module fails if the library has not been built
 (``python -m block_scale_search_amd.build``).
 
-The convenience wrappers at the end (``diag_hessian``, ``global_scale``, ``scale_search``,
-``pack``) allocate outputs and (zero-filled) workspaces with torch and call the entry points.
+The convenience wrappers at the end (``diag_hessian``, ``layer_statistics``, ``global_scale``,
+``scale_search``, ``scale_search_proposal``, ``pack``, ``quantize_activations``, ``gptq``,
+``output_error``) allocate outputs and workspaces with torch and call the entry points.
 """
 from __future__ import annotations
 
