@@ -4,7 +4,8 @@ relative, S exact).
 
 Cases: bf16 and f32 X and W in all four pairings, ragged token and column counts, X above the
 256 MiB size where the h pass switches to 4-wave workgroups, strided rows, accumulation into a
-running sum, empty token chunks, an all-zero W (S = 1) and both global-scale rules."""
+running sum, empty token chunks, an all-zero W (S = 1), both global-scale rules, and the full
+8B-shaped layers as the bench step runs them."""
 import numpy as np
 import pytest
 import torch
@@ -80,3 +81,21 @@ def test_accumulate_empty_chunk_and_zero_weights(nv):
     Wz = torch.zeros_like(W)
     acc3, _, S = _check(nv, X[:0], Wz, nv.GS_AMAX_256, acc=acc2, accumulate=True)
     assert torch.equal(acc3, acc2) and S.item() == 1.0
+
+
+@pytest.mark.parametrize("name", ["attn8b", "down8b"])
+def test_full_size_workloads(nv, name):
+    """The one-chunk workloads as the bench step runs them: bit-identical to the two calls, S
+    equal to the oracle's, h against the oracle on a sampled column block."""
+    cfg = workloads.CONFIGS[name]
+    W = workloads.make_weights(cfg, DEV)
+    sig = workloads.make_sigma(cfg, DEV)
+    X, _ = workloads.make_activation_chunk(cfg, sig, 0, DEV)
+    rule = nv.GS_AMAX_256 if cfg.gs_rule == "amax256" else nv.GS_AMAX_448
+    orule = oracle.GS_AMAX_256 if cfg.gs_rule == "amax256" else oracle.GS_AMAX_448
+    acc, h, S = _check(nv, X, W, rule)
+    assert S.item() == np.float32(oracle.global_scale(host_w(W), orule))
+    cols = slice(1024, 1024 + 256)
+    acc_o, h_o = oracle.diag_hessian(host_w(X[:, cols].contiguous()))
+    np.testing.assert_allclose(h[cols].cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    np.testing.assert_allclose(acc[cols].cpu().numpy(), acc_o, rtol=1e-12, atol=0)
