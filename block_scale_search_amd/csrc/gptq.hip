@@ -25,14 +25,16 @@
 //           zero, and the columns at or before j were stored when they were quantised). The
 //           chain through the errors is serial, so this kernel is latency-bound.
 //   update: after each outer block every later column takes its 256 updates as one fma chain
-//           in column order, acc = fma(-err_j, U[j][k], acc), on 128 x 128 tiles (8 x 8 per
-//           thread; 32 x 128 tiles when the columns are few) with the errors and U rows
+//           in column order, acc = fma(-err_j, U[j][k], acc), on 128-, 64- or 32-row x
+//           128-column tiles (8, 4 or 2 x 8 per thread, the height chosen so that the tiles
+//           fill the resident workgroups evenly) with the errors and U rows
 //           staged through LDS. Batching 256 errors per pass over the later columns keeps the
 //           pass bound by the fma issue rate rather than by HBM.
 // Each element of W sees exactly the sequential algorithm's fma sequence, so the result does
 // not depend on the blocking.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <utility>
 
 #include "device_formats.h"
@@ -401,8 +403,8 @@ struct UpdateArgs {
 };
 
 // Row of accumulator a of thread row ty in a tile of 16 TR rows: for TR = 8 rows 4ty + a and
-// 64 + 4ty + a - 4 (each LDS read of a wave then covers 256 contiguous bytes), for TR = 2 rows
-// 2ty + a.
+// 64 + 4ty + a - 4 (each LDS read of a wave then covers 256 contiguous bytes), for TR = 4 and
+// TR = 2 rows TR ty + a.
 template <int TR>
 __device__ __forceinline__ int tile_row(int ty, int a) {
     if constexpr (TR == 8) return a < 4 ? 4 * ty + a : 64 + 4 * ty + a - 4;
@@ -487,6 +489,9 @@ __device__ __forceinline__ void update_body(UpdateLds& L, uint32_t bx, uint32_t 
                 const float4 e1 = *reinterpret_cast<const float4*>(&es[jj][64 + 4 * ty]);
                 e[0] = e0.x; e[1] = e0.y; e[2] = e0.z; e[3] = e0.w;
                 e[4] = e1.x; e[5] = e1.y; e[6] = e1.z; e[7] = e1.w;
+            } else if constexpr (TR == 4) {
+                const float4 e0 = *reinterpret_cast<const float4*>(&es[jj][4 * ty]);
+                e[0] = e0.x; e[1] = e0.y; e[2] = e0.z; e[3] = e0.w;
             } else {
                 const float2 e0 = *reinterpret_cast<const float2*>(&es[jj][2 * ty]);
                 e[0] = e0.x; e[1] = e0.y;
@@ -538,15 +543,68 @@ UpdateArgs update_args(float* Wf, int64_t out, int64_t in, int64_t k0, int64_t k
 }
 
 // 128-row tiles where they give at least two workgroups per compute unit, else 32-row tiles
+// Resident update workgroups of each tile height on this device (compute units times
+// workgroups per compute unit), queried once per device.
+struct UpdateCapacity {
+    std::atomic<int64_t> cap[3] = {0, 0, 0};   // TR = 8, 4, 2
+};
+constexpr int kMaxDevices = 64;
+UpdateCapacity g_update_cap[kMaxDevices];
+
+template <int TR>
+int64_t resident(int cus) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_gptq_update<TR>, 256, 0) !=
+            hipSuccess ||
+        per_cu < 1)
+        per_cu = 1;
+    return (int64_t)per_cu * cus;
+}
+
+// Concurrent first calls may both fill an entry; they write the same values, and cap[0] is
+// stored last (release) and read first (acquire), so a reader sees a complete entry.
+void update_capacity(int64_t cap[3]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) dev = 0;
+    UpdateCapacity& c = g_update_cap[dev];
+    if (c.cap[0].load(std::memory_order_acquire) == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus < 1)
+            cus = 1;
+        c.cap[1].store(resident<4>(cus), std::memory_order_relaxed);
+        c.cap[2].store(resident<2>(cus), std::memory_order_relaxed);
+        c.cap[0].store(resident<8>(cus), std::memory_order_release);
+    }
+    cap[0] = c.cap[0].load(std::memory_order_acquire);
+    cap[1] = c.cap[1].load(std::memory_order_relaxed);
+    cap[2] = c.cap[2].load(std::memory_order_relaxed);
+}
+
+// Tile height by how evenly the tiles fill the resident workgroups: a grid of 1.25 rounds takes
+// as long as 2. Taller tiles read less LDS per fma, so each shorter height must win clearly
+// (weights 1, 0.92, 0.8).
 void launch_update(const UpdateArgs& p, hipStream_t stream) {
     if (p.k0 >= p.k1 || p.nj <= 0) return;
-    const uint32_t gy8 = (uint32_t)((p.out + 127) / 128);
-    if ((uint64_t)p.gx * gy8 >= 512) {
-        hipLaunchKernelGGL(k_gptq_update<8>, dim3(p.gx, gy8), dim3(256), 0, stream, p);
-    } else {
-        const dim3 grid(p.gx, (uint32_t)((p.out + 31) / 32));
-        hipLaunchKernelGGL(k_gptq_update<2>, grid, dim3(256), 0, stream, p);
+    int64_t cap[3];
+    update_capacity(cap);
+    const int trs[3] = {8, 4, 2};
+    const double weight[3] = {1.0, 0.92, 0.8};
+    int best = 0;
+    double best_score = -1.0;
+    for (int i = 0; i < 3; ++i) {
+        const int64_t tiles = (int64_t)p.gx * ((p.out + 16 * trs[i] - 1) / (16 * trs[i]));
+        const int64_t rounds = (tiles + cap[i] - 1) / cap[i];
+        const double score = weight[i] * (double)tiles / (double)(rounds * cap[i]);
+        if (score > best_score) {
+            best_score = score;
+            best = i;
+        }
     }
+    const dim3 grid(p.gx, (uint32_t)((p.out + 16 * trs[best] - 1) / (16 * trs[best])));
+    if (best == 0) hipLaunchKernelGGL(k_gptq_update<8>, grid, dim3(256), 0, stream, p);
+    else if (best == 1) hipLaunchKernelGGL(k_gptq_update<4>, grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL(k_gptq_update<2>, grid, dim3(256), 0, stream, p);
 }
 
 template <bool WMSE, int NWIN>
