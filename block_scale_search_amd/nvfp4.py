@@ -273,6 +273,10 @@ def nvfp4_gptq(W, out, inp, ldw, U, h, objective, lo, hi, S, scales, packed, W_f
     _need(scales, out * (inp // 16), "scales")
     _need(packed, out * (inp // 2), "packed")
     _need(U, inp * inp, "U")
+    if h is not None:
+        _need(h, inp, "h")
+    if W_final is not None:
+        _need(W_final, out * inp, "W_final")
     return _run("nvfp4_gptq", (
         _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), out, inp, ldw,
         _dev(U, "U", (torch.float32,)), _dev(h, "h", (torch.float32,)), objective, lo, hi,
