@@ -286,6 +286,7 @@ def cpu_baseline(cfg, layer, threads: int):
 
     t_h = t_s = 0.0
     passes = 0
+    first = []            # the first pass's oracle results, for the parity report
     t0 = time.perf_counter()
     while True:
         for W, X, S in mats:
@@ -296,22 +297,27 @@ def cpu_baseline(cfg, layer, threads: int):
             else:
                 acc, h = oracle.diag_hessian(X, None, threads=threads)
             b = time.perf_counter()
-            oracle.global_scale(W, rule)
+            S_o = oracle.global_scale(W, rule)
+            res = []
             for m in cfg.modes:
                 wm = m.objective == "wmse"
                 if m.proposal:
-                    oracle.scale_search_proposal(W, h if wm else None,
-                                                 oracle.WMSE if wm else oracle.MSE, m.lo, m.hi,
-                                                 center, incoming, S, threads=threads)
+                    res.append(oracle.scale_search_proposal(
+                        W, h if wm else None, oracle.WMSE if wm else oracle.MSE, m.lo, m.hi,
+                        center, incoming, S_o, threads=threads))
                 else:
-                    oracle.scale_search(W, h if wm else None, oracle.WMSE if wm else oracle.MSE,
-                                        m.lo, m.hi, m.exhaustive, S, threads=threads)
+                    res.append(oracle.scale_search(
+                        W, h if wm else None, oracle.WMSE if wm else oracle.MSE, m.lo, m.hi,
+                        m.exhaustive, S_o, threads=threads))
             c = time.perf_counter()
             t_h += b - a
             t_s += c - b
+            if passes == 0:
+                first.append((h, S_o, [r_["scales"] for r_ in res]))
         passes += 1
         if time.perf_counter() - t0 >= 10.0:
             break
+    parity = parity_on_sample(cfg, layer, first)
     step_s = (t_h * tok_frac + t_s * w_frac) / passes
     searched = cfg.n_weights * len(cfg.modes)
     return {"value": searched / step_s, "unit": "weights/s", "cores": threads, "kind": "oracle",
@@ -319,7 +325,37 @@ def cpu_baseline(cfg, layer, threads: int):
                       f"h + global scale + {' + '.join(m.label for m in cfg.modes)}, "
                       f"{passes} passes in {time.perf_counter() - t0:.1f} s on {threads} threads; "
                       f"projected to the whole step (h time x {tok_frac:.3g}, "
-                      f"search time x {w_frac:.3g})"}
+                      f"search time x {w_frac:.3g})",
+            "parity_on_sample": parity}
+
+
+def parity_on_sample(cfg, layer, first):
+    """The GPU's own outputs of the timed steps against the oracle's first pass on the sampled
+    rows or experts: h (max relative difference), S (equal or not), and for each mode the
+    fraction of groups whose scale byte differs. The GPU searches used the GPU's h, the oracle
+    its own, so a WMSE mode's fraction is the flip fraction that h's rounding can cause (0 when
+    every h element agrees). Skipped for token-chunked workloads (the oracle sample holds one
+    chunk)."""
+    import numpy as np
+    if len(layer.chunks) != 1:
+        return {"note": "not computed: the oracle sample holds one token chunk of several"}
+    hg = layer.h.cpu().numpy().reshape(cfg.batch, cfg.inp)
+    Sg = layer.S.cpu().numpy().reshape(-1)
+    gpr = cfg.inp // 16
+    sc = [x.cpu().numpy().reshape(cfg.batch, cfg.out, gpr) for x in layer.scales]
+    h_rel, s_eq, mism, groups = 0.0, True, [0] * len(cfg.modes), 0
+    for e, (h_o, S_o, scales_o) in enumerate(first):
+        ho = np.asarray(h_o, dtype=np.float64).reshape(-1)
+        d = np.abs(hg[e].astype(np.float64) - ho) / np.maximum(np.abs(ho), 1e-30)
+        h_rel = max(h_rel, float(d.max()))
+        s_eq = s_eq and bool(np.float32(S_o) == Sg[e])
+        for mi, so in enumerate(scales_o):
+            so = np.asarray(so).reshape(-1, gpr)
+            mism[mi] += int((sc[mi][e][:so.shape[0]] != so).sum())
+        groups += np.asarray(scales_o[0]).size
+    return {"groups": groups, "h_max_rel_diff": h_rel, "S_equal": s_eq,
+            "scale_mismatch_fraction": {m.label: mism[i] / max(1, groups)
+                                        for i, m in enumerate(cfg.modes)}}
 
 
 def read_traffic(workload: str, kernel_label: str):
