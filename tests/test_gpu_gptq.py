@@ -129,3 +129,10 @@ def test_gptq_full_size_sampled_rows(nv, name, lo, hi):
     wf = g["W_final"][torch.from_numpy(rows).to(DEV)].cpu().numpy()
     bad = np.argwhere(wf.view(np.uint32) != o["W_final"].view(np.uint32))
     assert bad.size == 0, f"{name} W_final: {len(bad)} mismatches, first {bad[:3].tolist()}"
+
+
+@pytest.mark.parametrize("out,inp", [(1, 16), (3, 48), (17, 64), (16, 80)])
+def test_gptq_small_shapes(nv, out, inp):
+    """One group, partial inner blocks and single rows."""
+    W, U, h = _case(out, inp, torch.bfloat16, seed=211 + inp, T=256)
+    _compare(nv, W, U, h, "wmse", -9, 6)
