@@ -94,17 +94,6 @@ __device__ __forceinline__ int row_argmin(float L, int c) {
     return c;
 }
 
-// Workgroup barrier for LDS reuse only: waits for this wave's LDS accesses (lgkmcnt(0); the
-// vmcnt and expcnt fields at their maxima) and not for its global stores, which drain in the
-// background (nothing in the kernel reads them back). __syncthreads would also wait for the
-// previous inner block's stores, several microseconds per block.
-__device__ __forceinline__ void lds_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
 constexpr int kOB = 256;        // columns per outer block
 constexpr int kBlockRows = 16;  // rows per block-kernel workgroup (256 threads)
 
@@ -329,7 +318,7 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
     load_u(0);
     for (int ib = 0; ib * kB < oc; ++ib) {
         const int bc = min(kB, oc - ib * kB);
-        lds_barrier();                                  // the previous inner block's readers
+        __syncthreads();                                // the previous inner block's readers
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
             const int J = (tid >> 6) + 4 * q;
@@ -345,7 +334,7 @@ __device__ __forceinline__ void outer_body(OuterLds& L, uint32_t rg, const Outer
             }
             L.us[J][sl_t][tt_t] = v;
         }
-        lds_barrier();
+        __syncthreads();
         // the previous inner block's results, stored only now: a store still in flight at the
         // staging above would have been waited for with the prefetched loads
         if (ib > 0) store_block(ib - 1);
