@@ -20,6 +20,9 @@
 // sum over all chunks.
 // The kernel boundary makes the partials of every XCD visible to the finalize kernel.
 // HBM traffic: X once plus 16 B per column per row group (partial written and read back).
+// Layer statistics (one matrix, one chunk): the same two passes with the global scale's amax
+// pass (amax_device.h) as a second workgroup role of the partial launch and the S computation
+// as one more workgroup of the finalize launch.
 #include <hip/hip_runtime.h>
 
 #include "amax_device.h"
