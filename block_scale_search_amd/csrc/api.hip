@@ -368,7 +368,7 @@ nvfp4_status nvfp4_output_error(const void* X, int x_dtype, int64_t tokens, int6
     nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
     if (st != NVFP4_OK) return st;
     if (tokens < 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
-    if (((out + 127) / 128) * ((tokens + 255) / 256) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
+    if (nvfp4::output_error_tiles(tokens, out) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
     if (out == 0) return NVFP4_OK;
     if (err == nullptr) return NVFP4_ERR_NULL;
     if (reinterpret_cast<uintptr_t>(err) & 7u) return NVFP4_ERR_ALIGN;

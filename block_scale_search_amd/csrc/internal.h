@@ -78,6 +78,7 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
 
 // Layer-output error: workspace bytes (residual halves + token-tile partials) and launch.
 size_t output_error_workspace_bytes(int64_t tokens, int64_t out, int64_t in);
+int64_t output_error_tiles(int64_t tokens, int64_t out);   // GEMM workgroups
 hipError_t launch_output_error(const void* X, int64_t tokens, int64_t in, int64_t ldx,
                                const void* W, bool w_bf16, int64_t out, int64_t ldw,
                                const uint8_t* scales, const uint8_t* packed, const float* S,

@@ -325,7 +325,7 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
  *           (token chunks of one calibration set).
  * workspace device, at least nvfp4_output_error_workspace_size(tokens, out, in) bytes,
  *           16-byte aligned, no initialisation needed (holds E_hi, E_lo and the tile partials).
- * Requires in % 16 == 0 and ceil(out/128) * ceil(tokens/256) < 2^31. tokens == 0 or in == 0
+ * Requires in % 16 == 0 and ceil(out/256) * ceil(tokens/256) < 2^31. tokens == 0 or in == 0
  * only writes err.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_output_error_workspace_size(int64_t tokens, int64_t out, int64_t in);

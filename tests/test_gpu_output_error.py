@@ -46,7 +46,7 @@ def _check(nv, X, W, S, packed, scales, rows=None, what=""):
 
 @pytest.mark.parametrize("w_dtype", [torch.bfloat16, torch.float32])
 def test_output_error_ragged(nv, w_dtype):
-    """Token count, row count and column count off the 128/128/32 tiles; padded X rows."""
+    """Token count, row count and column count off the 256/256/32 tiles; padded X rows."""
     W, X = _case(300, 150, 272, w_dtype, seed=101, ldx=280)
     W[5] = 0.0                                                   # a zero row: exactly 0
     S = nv.global_scale(W, nv.GS_AMAX_448)
@@ -54,6 +54,16 @@ def test_output_error_ragged(nv, w_dtype):
         r = nv.scale_search(W, None, S, nv.MSE, lo, hi, with_stats=False)
         e, o = _check(nv, X, W, S, r["packed"], r["scales"], what=f"[{lo},{hi}] {w_dtype}")
         assert e[5] == 0.0
+
+
+@pytest.mark.parametrize("T,out,inp", [(700, 600, 1040), (1024, 2048, 256), (256, 256, 32)])
+def test_output_error_tiles(nv, T, out, inp):
+    """Several 256 x 256 tiles: ragged in every dimension (K ending on half a 32-wide step),
+    the XCD-grouped tile order (4 x 8 tiles), and exactly one tile with one K step."""
+    W, X = _case(T, out, inp, torch.bfloat16, seed=107 + inp)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    r = nv.scale_search(W, None, S, nv.MSE, -3, 7, with_stats=False)
+    _check(nv, X, W, S, r["packed"], r["scales"], what=f"{T}x{out}x{inp}")
 
 
 def test_output_error_zero_residual_is_exactly_zero(nv):
