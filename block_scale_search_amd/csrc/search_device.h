@@ -27,12 +27,19 @@
 
 namespace nvfp4 {
 
-// Loss of one code: the weighted squares in element order, L = u0 * d0, then
-// L = fma(u_j, d_j, L) for j = 1..15.
+// Loss of one code: the weighted squares summed in a fixed tree. For each quad k = 0..3,
+// P_k = u_4k * d_4k, then P_k = fma(u_4k+i, d_4k+i, P_k) for i = 1, 2, 3; the loss is
+// (P_0 + P_1) + (P_2 + P_3).
+__device__ __forceinline__ float quad_tree(const float (&P)[4]) {
+    const float left = P[0] + P[1];
+    const float right = P[2] + P[3];
+    return left + right;
+}
+
 template <bool WMSE>
 __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)[16], float eff,
                                           float r) {
-    float L = 0.0f;
+    float P[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         float x[8], q[8];
@@ -45,10 +52,10 @@ __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)
             const float a = fabsf(w[j]);
             const float d = __builtin_fmaf(-q[i], eff, a);
             const float u = WMSE ? h[j] * d : d;
-            L = (j == 0) ? u * d : __builtin_fmaf(u, d, L);
+            P[j >> 2] = (j & 3) == 0 ? u * d : __builtin_fmaf(u, d, P[j >> 2]);
         }
     }
-    return L;
+    return quad_tree(P);
 }
 
 // Losses of codes c and c + 8 from one multiply per element (valid when both are normal codes
@@ -56,7 +63,7 @@ __device__ __forceinline__ float loss_one(const float (&w)[16], const float (&h)
 template <bool WMSE>
 __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)[16], float eff,
                                           float r, float eff_hi, float& L_lo, float& L_hi) {
-    float P = 0.0f, Q = 0.0f;
+    float P[4], Q[4];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
         float x[8], q[8], s[8];
@@ -72,12 +79,12 @@ __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)
             const float e = __builtin_fmaf(-s[i], eff_hi, a);
             const float u = WMSE ? h[j] * d : d;
             const float v = WMSE ? h[j] * e : e;
-            P = (j == 0) ? u * d : __builtin_fmaf(u, d, P);
-            Q = (j == 0) ? v * e : __builtin_fmaf(v, e, Q);
+            P[j >> 2] = (j & 3) == 0 ? u * d : __builtin_fmaf(u, d, P[j >> 2]);
+            Q[j >> 2] = (j & 3) == 0 ? v * e : __builtin_fmaf(v, e, Q[j >> 2]);
         }
     }
-    L_lo = P;
-    L_hi = Q;
+    L_lo = quad_tree(P);
+    L_hi = quad_tree(Q);
 }
 
 // Running minimum over candidates visited in ascending code order: a strictly smaller loss
@@ -210,7 +217,7 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
 // Each lane first scores the 16 codes around its own base code (octave pairs when the table
 // allows), then extends upward and downward in blocks of 8 codes while the loss bounds above
 // cannot exclude the next code. A bound prunes a direction when it exceeds the best loss by a
-// relative margin of 2^-14, which covers the rounding of the binary32 loss chain and of the
+// relative margin of 2^-14, which covers the rounding of the binary32 loss tree and of the
 // bound itself (each at most about 20 roundings of 2^-24 on sums of non-negative terms). The
 // test is used only where that error analysis holds: non-negative finite h, a best loss of at
 // least 2^-100 and amax (1 + max h) <= 2^100 best, so that underflowing products (absolute

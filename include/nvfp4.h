@@ -169,8 +169,9 @@ nvfp4_status nvfp4_layer_statistics(const void* X, int x_dtype, int64_t tokens, 
  *            WMSE in FP8 bit-pattern space), or all codes 1..126 if exhaustive ([SS] §2)
  *   loss(c) = sum_j u_j * d_j, x_j = fl(|w_j| * r[c]), q_j = E2M1_RNE(x_j) (ties to the even
  *            code, saturating at 6), d_j = fma(-q_j, eff[c], |w_j|), u_j = fl(h_j * d_j) for
- *            WMSE or d_j for MSE, summed in element order in binary32: L = u_0 d_0, then
- *            L = fma(u_j, d_j, L) for j = 1..15
+ *            WMSE or d_j for MSE, summed in binary32 in a fixed tree: per quad k = 0..3,
+ *            P_k = u_4k d_4k, then P_k = fma(u_4k+i, d_4k+i, P_k) for i = 1..3;
+ *            L = (P_0 + P_1) + (P_2 + P_3)
  *   choice = the code of smallest loss, the lowest code among equal losses ([SR] App. D.2:
  *            ties are deterministic)
  *   output ([HS] App. B: quantize once with the chosen scale, native NVFP4):

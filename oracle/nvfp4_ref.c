@@ -29,8 +29,9 @@
  *     or a caller-given S. S = 1 for an all-zero tensor.
  *   - Effective scale eff[c] = fl(S * dec(c)); its reciprocal r[c] = fl(1 / eff[c]); a weight is
  *     normalised as fl(|w| * r[c]).
- *   - Residual d = fma(-q, eff, |w|); the weighted squares are summed with fmas in element
- *     order; the first strictly smaller loss wins, so ties go to the lowest offset.
+ *   - Residual d = fma(-q, eff, |w|); the weighted squares are summed in a fixed tree: four
+ *     fma chains over the element quads 4k..4k+3, then (P0 + P1) + (P2 + P3); the first
+ *     strictly smaller loss wins, so ties go to the lowest offset.
  *   - Nibble = sign(w) << 3 | E2M1 index; two nibbles per byte, low nibble first.
  */
 #include <math.h>
@@ -182,19 +183,25 @@ int ref_scale_tables(float S, float* eff, float* rcp)
  * reconstruction objective; [SS] §1: MSE and WMSE). For element j:
  *   x_j = fl(|w_j| * r),  q_j = E2M1(x_j),  d_j = fma(-q_j, eff, |w_j|),
  *   u_j = fl(h_j * d_j) (WMSE) or d_j (MSE).
- * The 16 products u_j * d_j are summed in element order: L = fl(u_0 * d_0), then
- * L = fma(u_j, d_j, L) for j = 1..15. */
+ * The 16 products u_j * d_j are summed in a fixed tree: for each quad k = 0..3,
+ * P_k = fl(u_4k * d_4k), then P_k = fma(u_4k+i, d_4k+i, P_k) for i = 1, 2, 3;
+ * L = fl(fl(P_0 + P_1) + fl(P_2 + P_3)). */
 static float group_loss(const float a[16], const float* h, float eff, float r)
 {
-    float L = 0.0f;
-    for (int j = 0; j < 16; ++j) {
-        float x = a[j] * r;
-        float q = E2M1_LEVEL[ref_e2m1_index(x)];
-        float d = fmaf(-q, eff, a[j]);
-        float u = h ? h[j] * d : d;
-        L = (j == 0) ? u * d : fmaf(u, d, L);
+    float P[4];
+    for (int k = 0; k < 4; ++k) {
+        for (int i = 0; i < 4; ++i) {
+            int j = 4 * k + i;
+            float x = a[j] * r;
+            float q = E2M1_LEVEL[ref_e2m1_index(x)];
+            float d = fmaf(-q, eff, a[j]);
+            float u = h ? h[j] * d : d;
+            P[k] = (i == 0) ? u * d : fmaf(u, d, P[k]);
+        }
     }
-    return L;
+    float left = P[0] + P[1];
+    float right = P[2] + P[3];
+    return left + right;
 }
 
 /* Base code of a group: the E4M3-rounded absmax/6 in units of S ([SS] Problem Statement and §2:
