@@ -1,0 +1,65 @@
+"""GPU parity over seeded random configurations: shapes, dtypes, batch counts, padded rows,
+objectives, windows (including one-sided and wide ones), exhaustive mode, both global-scale
+rules, weight scales over twelve decades, heavy tails, zero and subnormal-range groups, and h
+with zeros and a wide spread. Every output is compared with the oracle bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import DEV, assert_same, gpu_search, host_w, oracle_search
+
+pytestmark = pytest.mark.gpu
+
+N_CASES = 24
+
+
+def _case(i: int):
+    rng = np.random.default_rng(9000 + i)
+    batch = int(rng.choice([1, 1, 2, 3]))
+    out = int(rng.integers(1, 200))
+    inp = 16 * int(rng.integers(1, 40))
+    pad = 8 * int(rng.integers(0, 3))
+    dtype = torch.bfloat16 if rng.random() < 0.6 else torch.float32
+    scale = float(10.0 ** rng.uniform(-6, 3))
+    kind = rng.choice(["normal", "student", "sparse", "outlier"])
+    w = rng.standard_normal((batch, out, inp))
+    if kind == "student":
+        w = rng.standard_t(3, (batch, out, inp))
+    elif kind == "sparse":
+        w[rng.random(w.shape) < 0.6] = 0.0
+    elif kind == "outlier":
+        w[rng.random(w.shape) < 0.01] *= 40.0
+    w = w * scale
+    zero_rows = rng.random(out) < 0.05                       # whole zero rows: zero groups
+    w[:, zero_rows, :] = 0.0
+    buf = torch.zeros((batch, out, inp + pad), dtype=torch.float32)
+    buf[:, :, :inp] = torch.from_numpy(w.astype(np.float32))
+    buf[:, :, inp:] = 1e30 if dtype == torch.float32 else 3e38   # padding must not matter
+    W = buf.to(dtype).to(DEV)[:, :, :inp]
+    h = np.exp(rng.standard_normal((batch, inp)) * float(rng.uniform(0.5, 4.0))).astype(np.float32)
+    h[rng.random(h.shape) < 0.1] = 0.0
+    if batch == 1:
+        W, h = W[0], h[0]
+    objective = "wmse" if rng.random() < 0.6 else "mse"
+    exhaustive = bool(rng.random() < 0.15)
+    lo = -int(rng.integers(0, 20)) if rng.random() < 0.8 else -int(rng.integers(0, 126))
+    hi = int(rng.integers(0, 20)) if rng.random() < 0.8 else int(rng.integers(0, 126))
+    rule = int(rng.integers(0, 2))
+    return W, h, objective, lo, hi, exhaustive, rule
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_random_configuration(nv, i):
+    W, h, objective, lo, hi, exhaustive, rule = _case(i)
+    S = nv.global_scale(W, nv.GS_AMAX_448 if rule == 0 else nv.GS_AMAX_256)
+    Wn = host_w(W)
+    Wb = Wn if Wn.ndim == 3 else Wn[None]
+    S_o = [oracle.global_scale(Wb[b], oracle.GS_AMAX_448 if rule == 0 else oracle.GS_AMAX_256)
+           for b in range(Wb.shape[0])]
+    assert np.array_equal(S.cpu().numpy().reshape(-1), np.float32(S_o)), f"case {i}: S"
+    ht = torch.from_numpy(h).to(DEV) if objective == "wmse" else None
+    g = gpu_search(nv, W, ht, S, objective, lo, hi, exhaustive)
+    o = oracle_search(W, h if objective == "wmse" else None, S_o if len(S_o) > 1 else S_o[0],
+                      objective, lo, hi, exhaustive)
+    assert_same(g, o, f"case {i}: {tuple(W.shape)} {W.dtype} {objective} [{lo},{hi}] exh={exhaustive}")
