@@ -11,6 +11,8 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -47,12 +49,7 @@ def _torch_hip_dir() -> str | None:
     return d if os.path.exists(os.path.join(d, "libamdhip64.so")) else None
 
 
-def build(verbose: bool = False) -> str:
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    cmd = [_hipcc(), *HIP_FLAGS, "-o", LIB + ".tmp", *srcs]
-    tdir = _torch_hip_dir()
-    if tdir:
-        cmd += [f"-L{tdir}", f"-Wl,-rpath,{tdir}"]
+def _run(cmd: list[str], verbose: bool) -> list[str]:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -60,8 +57,31 @@ def build(verbose: bool = False) -> str:
     msgs = [l for l in (res.stdout + res.stderr).splitlines() if noise not in l and l.strip()]
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
-    if verbose and msgs:
-        print("\n".join(msgs))
+    return msgs
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source to an object (in parallel, into a fresh private folder), then link
+    the shared library. Every call compiles everything."""
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    hipcc = _hipcc()
+    compile_flags = [f for f in HIP_FLAGS if f != "-shared"]
+    os.makedirs(os.path.join(HERE, "_build"), exist_ok=True)
+    with tempfile.TemporaryDirectory(dir=os.path.join(HERE, "_build")) as objdir:
+        objs = [os.path.join(objdir, os.path.basename(src) + ".o") for src in srcs]
+        jobs = max(1, min(len(srcs), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(max_workers=jobs) as pool:
+            msgs = list(pool.map(lambda so: _run([hipcc, *compile_flags, "-c", so[0], "-o", so[1]],
+                                                 verbose), zip(srcs, objs)))
+        cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", LIB + ".tmp", *objs]
+        tdir = _torch_hip_dir()
+        if tdir:
+            cmd += [f"-L{tdir}", f"-Wl,-rpath,{tdir}"]
+        msgs.append(_run(cmd, verbose))
+    if verbose:
+        for m in msgs:
+            if m:
+                print("\n".join(m))
     os.replace(LIB + ".tmp", LIB)
     return LIB
 
