@@ -337,6 +337,40 @@ def cpu_baseline(cfg, layer, threads: int):
             "parity_on_sample": parity}
 
 
+def cpu_single_core(cfg, layer):
+    """The oracle on one host thread, for the single-matrix workloads up to 2^26 weights: one pass
+    over about 2^20 weights (whole rows) and at most 2048 tokens, projected to the whole step by
+    the weight and token ratios."""
+    import numpy as np
+
+    import oracle
+
+    if cfg.batch != 1 or cfg.n_weights > (1 << 26):
+        return None
+    R = max(1, min(cfg.out, (1 << 20) // cfg.inp))
+    W = host_array(layer.W[:R])
+    X = host_array(layer.chunks[0][:2048])
+    rule = oracle.GS_AMAX_256 if cfg.gs_rule == "amax256" else oracle.GS_AMAX_448
+    S_whole = oracle.global_scale(host_array(layer.W), rule)
+    a = time.perf_counter()
+    _, h = oracle.diag_hessian(X, None, threads=1)
+    b = time.perf_counter()
+    oracle.global_scale(W, rule)
+    for m in cfg.modes:
+        wm = m.objective == "wmse"
+        if m.proposal:
+            continue
+        oracle.scale_search(W, h if wm else None, oracle.WMSE if wm else oracle.MSE, m.lo, m.hi,
+                            m.exhaustive, S_whole, threads=1)
+    c = time.perf_counter()
+    tok_frac = cfg.tokens / X.shape[0]
+    w_frac = cfg.out / R
+    step_s = (b - a) * tok_frac + (c - b) * w_frac
+    return {"value": cfg.n_weights * len(cfg.modes) / step_s, "unit": "weights/s", "cores": 1,
+            "sample": f"{R} of {cfg.out} rows and {X.shape[0]} of {cfg.tokens} tokens, one pass, "
+                      f"projected (h time x {tok_frac:.3g}, search time x {w_frac:.3g})"}
+
+
 def parity_on_sample(cfg, layer, first):
     """The GPU's own outputs of the timed steps against the oracle's first pass on the sampled
     rows or experts: h (max relative difference), S (equal or not), and for each mode the
@@ -726,6 +760,9 @@ def main():
     if not args.no_cpu:
         threads = min(16, len(os.sched_getaffinity(0)))
         cpu = cpu_baseline(cfg, runner.sets[0], threads)
+        one = cpu_single_core(cfg, runner.sets[0])
+        if one is not None:
+            cpu["single_core"] = one
 
     # the h stage of a step: every chunk's call plus the deferred finalize, over X's bytes; with
     # the fused call, h and S together over the bytes of X and W
