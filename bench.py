@@ -2,7 +2,9 @@
 
 One step = the whole path over one synthetic layer held in HBM:
   diagonal Hessian over X -> global scale of W -> scale search + pack for every mode the
-  workload names (attn8b: MSE [-3,7] and WMSE [-8,7]).
+  workload names (attn8b: MSE [-3,7] and WMSE [-8,7]). Two windowed modes of 11 or 16 codes on
+  bf16 W run as one nvfp4_scale_search_rules call, whose paired launch reads each group once
+  for both (--separate-searches times one nvfp4_scale_search call per mode).
 On workloads of one matrix and one token chunk, h and S come from one call
 (nvfp4_layer_statistics, two launches; --separate-stats times the two separate calls).
 With --streams 2 the h-reduce runs on a second stream (same default priority), overlapping the
@@ -115,6 +117,7 @@ class Runner:
         self.ws_ls = torch.zeros(max(16, nvfp4.nvfp4_layer_statistics_workspace_size(
             T, cfg.inp, cfg.out)), dtype=torch.uint8, device=dev)
         self.separate_stats = False
+        self.separate_searches = False
         self.rule = nvfp4.GS_AMAX_256 if cfg.gs_rule == "amax256" else nvfp4.GS_AMAX_448
         if any(m.proposal for m in cfg.modes):
             # proposal and incoming codes, made once outside the timed steps: the incoming code is
@@ -170,8 +173,21 @@ class Runner:
         if not fused:
             out.append(("global_scale", nv.nvfp4_global_scale(
                 s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
+        pair = None if self.separate_searches else paired_modes(cfg)
+        if pair is not None:
+            # two windowed rules in one call: one launch reads each group once for both
+            idx = [cfg.modes.index(m) for m in pair]
+            wm_any = any(m.objective == "wmse" for m in pair)
+            rules = [dict(objective=nv.WMSE if m.objective == "wmse" else nv.MSE, lo=m.lo,
+                          hi=m.hi, exhaustive=False, scales=s.scales[i], packed=s.packed[i])
+                     for m, i in zip(pair, idx)]
+            out.append((pair_label(pair), nv.nvfp4_scale_search_rules(
+                s.W, b, o, n, ldw, sw, 16, s.h if wm_any else None, n if wm_any else 0, s.S,
+                rules, prepare=True), "main_after_h" if wm_any else "main"))
         for mi, m in enumerate(cfg.modes):
             wm = m.objective == "wmse"
+            if pair is not None and m in pair:
+                continue
             if m.proposal:
                 out.append((f"search:{m.label}", nv.nvfp4_scale_search_proposal(
                     s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
@@ -188,12 +204,35 @@ class Runner:
         return sorted(out, key=lambda t: rank[t[2]])
 
 
+def paired_modes(cfg):
+    """The step's two windowed modes when they run as one nvfp4_scale_search_rules call with a
+    paired launch (bf16 W, exactly two plain windows of 11 or 16 codes), else None."""
+    plain = [m for m in cfg.modes if not m.proposal]
+    if len(plain) != 2 or len(plain) != len(cfg.modes):
+        return None
+    if not str(cfg.w_dtype).endswith("bfloat16"):
+        return None
+    if any(m.exhaustive or n_candidates(m) not in (11, 16) for m in plain):
+        return None
+    return plain
+
+
+def pair_label(modes) -> str:
+    return "search:" + "+".join(m.label for m in modes)
+
+
+def label_modes(cfg, label: str):
+    """The modes a search label covers ("search:A" or "search:A+B"), else []."""
+    if not label.startswith("search:"):
+        return []
+    parts = label[len("search:"):].split("+")
+    return [m for p in parts for m in cfg.modes if m.label == p]
+
+
 def algorithmic_ops(cfg, label: str) -> int:
     """VALU lane-operations a search call needs by the method's definition (0 for others)."""
-    mode = next((m for m in cfg.modes if label == f"search:{m.label}"), None)
-    if mode is None:
-        return 0
-    return cfg.n_weights * n_candidates(mode) * OPS_PER_ELEM_CAND[mode.objective]
+    return sum(cfg.n_weights * n_candidates(m) * OPS_PER_ELEM_CAND[m.objective]
+               for m in label_modes(cfg, label))
 
 
 def algorithmic(cfg, label: str):
@@ -210,11 +249,14 @@ def algorithmic(cfg, label: str):
     if label == "h_reduce+global_scale":
         T = cfg.chunk_tokens or cfg.tokens
         return T * cfg.inp * 2 + cfg.inp * 12 + n_w * wb + 4, 2 * T * cfg.inp + n_w
-    mode = next(m for m in cfg.modes if label == f"search:{m.label}")
-    bytes_ = n_w * wb + n_w // 2 + n_w // 16 + (cfg.batch * cfg.inp * 4 if mode.objective == "wmse" else 0)
-    if mode.proposal:
+    # a search call reads W (and h) once and writes each mode's codes and scale bytes
+    modes = label_modes(cfg, label)
+    bytes_ = n_w * wb + len(modes) * (n_w // 2 + n_w // 16)
+    if any(m.objective == "wmse" for m in modes):
+        bytes_ += cfg.batch * cfg.inp * 4
+    if any(m.proposal for m in modes):
         bytes_ += 2 * (n_w // 16)      # proposal and incoming code per group
-    flops = n_w * n_candidates(mode) * FLOPS_PER_ELEM_CAND[mode.objective]
+    flops = sum(n_w * n_candidates(m) * FLOPS_PER_ELEM_CAND[m.objective] for m in modes)
     return bytes_, flops
 
 
@@ -422,6 +464,9 @@ def main():
     ap.add_argument("--separate-stats", action="store_true",
                     help="h and S as two calls (nvfp4_diag_hessian, nvfp4_global_scale) instead "
                          "of nvfp4_layer_statistics on one-chunk workloads")
+    ap.add_argument("--separate-searches", action="store_true",
+                    help="one nvfp4_scale_search call per mode instead of one "
+                         "nvfp4_scale_search_rules call for a pair of windowed modes")
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: h-reduce on a second stream, overlapping the global scale and the "
                          "searches that do not read h")
@@ -457,6 +502,7 @@ def main():
           flush=True)
     runner = Runner(cfg, n_sets, dev)
     runner.separate_stats = args.separate_stats
+    runner.separate_searches = args.separate_searches
     torch.cuda.synchronize()
 
     if args.calib_copy:
@@ -713,7 +759,7 @@ def main():
              "alg_bytes": nb, "GB/s": round(nb / us_avg / 1e3, 1),
              "frac_hbm": round(nb / us_avg / 1e3 / HBM_PEAK_GBS, 4)}
         if lab.startswith("search"):
-            k["weights/s"] = cfg.n_weights / (us_avg * 1e-6)
+            k["weights/s"] = cfg.n_weights * len(label_modes(cfg, lab)) / (us_avg * 1e-6)
             if "exhaustive" in lab:
                 # exact pruning skips candidates that provably lose, so the 126-candidate flop
                 # count over the time is an equivalent rate, not a roofline figure

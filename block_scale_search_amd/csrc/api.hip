@@ -224,6 +224,45 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
         offset, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_scale_search_rules(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                      int64_t in, int64_t ldw, int64_t stride_w,
+                                      int32_t group_size, const float* h, int64_t stride_h,
+                                      const float* S, const nvfp4_search_rule* rules,
+                                      int32_t n_rules, void* stream) {
+    constexpr int kMaxRules = 64;
+    if (group_size != 16) return NVFP4_ERR_ARG;
+    if (rules == nullptr) return NVFP4_ERR_NULL;
+    if (n_rules < 1 || n_rules > kMaxRules) return NVFP4_ERR_ARG;
+    bool any_wmse = false;
+    for (int k = 0; k < n_rules; ++k) {
+        const nvfp4_search_rule& r = rules[k];
+        if (r.objective != NVFP4_MSE && r.objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
+        if (!r.exhaustive && (r.lo > 0 || r.hi < 0 || r.lo < -125 || r.hi > 125))
+            return NVFP4_ERR_WINDOW;
+        any_wmse = any_wmse || r.objective == NVFP4_WMSE;
+    }
+    nvfp4_status st = check_weights(W, w_dtype, batch, out, in, ldw, stride_w);
+    if (st != NVFP4_OK) return st;
+    if (any_wmse) {
+        if (stride_h < 0 || (batch > 1 && stride_h < in) || stride_h % 4 != 0) return NVFP4_ERR_SHAPE;
+    }
+    if (batch == 0 || out == 0 || in == 0) return NVFP4_OK;
+    if (S == nullptr || (any_wmse && h == nullptr)) return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(S) & 3u) || (any_wmse && !aligned16(h))) return NVFP4_ERR_ALIGN;
+    nvfp4::SearchRule rs[kMaxRules];
+    for (int k = 0; k < n_rules; ++k) {
+        const nvfp4_search_rule& r = rules[k];
+        if (r.scales == nullptr || r.packed == nullptr) return NVFP4_ERR_NULL;
+        if (!aligned8(r.packed) || (r.loss && (reinterpret_cast<uintptr_t>(r.loss) & 3u)))
+            return NVFP4_ERR_ALIGN;
+        rs[k] = nvfp4::SearchRule{r.objective == NVFP4_WMSE, r.lo, r.hi, r.exhaustive != 0,
+                                  nvfp4::RuleOut{r.scales, r.packed, r.loss, r.offset}};
+    }
+    return hip_status(nvfp4::launch_scale_search_rules(
+        W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw, stride_w, any_wmse ? h : nullptr,
+        any_wmse ? stride_h : 0, S, rs, n_rules, static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_scale_search_proposal(const void* W, int w_dtype, int64_t batch, int64_t out,
                                          int64_t in, int64_t ldw, int64_t stride_w,
                                          int32_t group_size, const float* h, int64_t stride_h,

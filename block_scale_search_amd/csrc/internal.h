@@ -76,6 +76,26 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
                                const uint8_t* center, const uint8_t* incoming,
                                hipStream_t stream);
 
+// Several search rules over one set of weights: each rule's outputs equal launch_scale_search's
+// for that rule alone. Consecutive windowed rules of 11 or 16 codes on bf16 W run in pairs, one
+// launch per pair sharing each group's loads, table and base code; the rest run one launch each.
+struct RuleOut {
+    uint8_t* scales;   // [batch, out, in/16]
+    uint8_t* packed;   // [batch, out, in/2]
+    float* loss;       // [batch, out, in/16] or null
+    int8_t* offset;    // [batch, out, in/16] or null
+};
+struct SearchRule {
+    bool wmse;
+    int lo, hi;
+    bool exhaustive;
+    RuleOut out;
+};
+hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, int64_t out,
+                                     int64_t in, int64_t ldw, int64_t stride_w, const float* h,
+                                     int64_t stride_h, const float* S, const SearchRule* rules,
+                                     int n_rules, hipStream_t stream);
+
 // Layer-output error: workspace bytes (residual halves + token-tile partials) and launch.
 size_t output_error_workspace_bytes(int64_t tokens, int64_t out, int64_t in);
 int64_t output_error_tiles(int64_t tokens, int64_t out);   // GEMM workgroups

@@ -8,7 +8,7 @@ there is no CPU path. Importing this module fails if the library has not been bu
 (``python -m block_scale_search_amd.build``).
 
 The convenience wrappers at the end (``diag_hessian``, ``layer_statistics``, ``global_scale``,
-``scale_search``, ``scale_search_proposal``, ``pack``, ``quantize_activations``, ``gptq``,
+``scale_search``, ``scale_search_rules``, ``scale_search_proposal``, ``pack``, ``quantize_activations``, ``gptq``,
 ``output_error``) allocate outputs and workspaces with torch and call the entry points.
 """
 from __future__ import annotations
@@ -30,6 +30,14 @@ GS_AMAX_448, GS_AMAX_256 = 0, 1
 
 _P, _I64, _I32, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_int, ctypes.c_size_t
 
+class SearchRule(ctypes.Structure):
+    """``nvfp4_search_rule``: one objective and window with its output pointers."""
+    _fields_ = [("objective", ctypes.c_int32), ("lo", ctypes.c_int32), ("hi", ctypes.c_int32),
+                ("exhaustive", ctypes.c_int32), ("scales", ctypes.c_void_p),
+                ("packed", ctypes.c_void_p), ("loss", ctypes.c_void_p),
+                ("offset", ctypes.c_void_p)]
+
+
 _SIGS = {
     "nvfp4_status_string": ([_I], ctypes.c_char_p),
     "nvfp4_version": ([], ctypes.c_char_p),
@@ -44,6 +52,8 @@ _SIGS = {
                                 _P, _SZ, _P], _I),
     "nvfp4_scale_search": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I, _I32, _I32, _I,
                             _P, _P, _P, _P, _P, _P], _I),
+    "nvfp4_scale_search_rules": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _P,
+                                  ctypes.POINTER(SearchRule), _I32, _P], _I),
     "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
                                      _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
@@ -212,6 +222,35 @@ def nvfp4_scale_search(W, batch, out, inp, ldw, stride_w, group_size, h, stride_
         _dev(S, "S", (torch.float32,)), _dev(scales, "scales", (torch.uint8,)),
         _dev(packed, "packed", (torch.uint8,)), _dev(loss, "loss", (torch.float32,)),
         _dev(offset, "offset", (torch.int8,)), _stream(stream)), prepare)
+
+
+def nvfp4_scale_search_rules(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h, S, rules,
+                             stream=None, prepare=False):
+    """rules: sequence of dicts with keys objective, lo, hi, exhaustive, scales, packed and
+    optionally loss, offset (tensors)."""
+    G = batch * out * (inp // 16)
+    _need(S, batch, "S")
+    arr = (SearchRule * len(rules))()
+    for k, r in enumerate(rules):
+        _need(r["scales"], G, "scales")
+        _need(r["packed"], G * 8, "packed")
+        loss, offset = r.get("loss"), r.get("offset")
+        if loss is not None:
+            _need(loss, G, "loss")
+        if offset is not None:
+            _need(offset, G, "offset")
+        p = lambda t, name, dt: None if t is None else _dev(t, name, dt).value
+        arr[k] = SearchRule(int(r["objective"]), int(r["lo"]), int(r["hi"]), int(r["exhaustive"]),
+                            p(r["scales"], "scales", (torch.uint8,)),
+                            p(r["packed"], "packed", (torch.uint8,)),
+                            p(loss, "loss", (torch.float32,)), p(offset, "offset", (torch.int8,)))
+    call = _run("nvfp4_scale_search_rules", (
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        group_size, _dev(h, "h", (torch.float32,)), stride_h, _dev(S, "S", (torch.float32,)),
+        arr, len(rules), _stream(stream)), prepare)
+    if prepare:
+        return lambda: (arr, call())[1]     # the closure keeps the rule array alive
+    return None
 
 
 def nvfp4_scale_search_proposal(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h,
@@ -393,6 +432,30 @@ def scale_search(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objec
     nvfp4_scale_search(W, b, o, n, ldw, sw, 16, h if objective == WMSE else None, stride_h,
                        objective, lo, hi, exhaustive, S, scales, packed, loss, offset, stream)
     return {"scales": scales, "packed": packed, "loss": loss, "offset": offset}
+
+
+def scale_search_rules(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, rules,
+                       with_stats: bool = True, stream=None) -> list[dict]:
+    """Several rules (objective, lo, hi, exhaustive) over W [out, in] or [batch, out, in] in one
+    call; returns one output dict per rule, as scale_search would."""
+    b, o, n, ldw, sw = _bmat(W)
+    shp = (o, n // 16) if W.dim() == 2 else (b, o, n // 16)
+    dev = W.device
+    outs, specs = [], []
+    for objective, lo, hi, exhaustive in rules:
+        r = {"scales": torch.empty(shp, dtype=torch.uint8, device=dev),
+             "packed": torch.empty(shp[:-1] + (n // 2,), dtype=torch.uint8, device=dev),
+             "loss": torch.empty(shp, dtype=torch.float32, device=dev) if with_stats else None,
+             "offset": torch.empty(shp, dtype=torch.int8, device=dev) if with_stats else None}
+        outs.append(r)
+        specs.append(dict(r, objective=objective, lo=lo, hi=hi, exhaustive=exhaustive))
+    wmse = any(objective == WMSE for objective, *_ in rules)
+    if wmse and h is None:
+        raise ValueError("WMSE needs h")
+    stride_h = (h.stride(0) if h.dim() == 2 else 0) if wmse else 0
+    nvfp4_scale_search_rules(W, b, o, n, ldw, sw, 16, h if wmse else None, stride_h, S, specs,
+                             stream)
+    return outs
 
 
 def scale_search_proposal(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objective: int,

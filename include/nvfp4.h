@@ -199,6 +199,40 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
                                 uint8_t* packed, float* loss, int8_t* offset, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * Steps 3-4 for several rules at once: the same weights searched under several objectives and
+ * windows, as when Min-Max, MSE-guided and Hessian-guided scales of one layer are compared
+ * ([HS] §4: MSE and Hessian-guided refinement against max-abs scales; [SS] §3: the MSE [-3, 7]
+ * and WMSE [-8, 7] windows of one model).
+ *
+ * rules[k]'s outputs are exactly those of nvfp4_scale_search with that rule's objective, lo, hi,
+ * exhaustive and output pointers, and the call's other arguments. Two consecutive windowed rules
+ * of 11 or 16 codes on bf16 W run as one launch that reads each group once and shares its
+ * table and base code between them; every other rule runs as its own launch.
+ *
+ * rules     host, n_rules entries (1 <= n_rules <= 64), read during the call only. The output
+ *           buffers of different rules must not overlap.
+ * h         required (with the alignment and stride of nvfp4_scale_search) if any rule is
+ *           WMSE; ignored otherwise.
+ * Every rule is validated before anything is enqueued; the first invalid rule's status is
+ * returned.
+ * ------------------------------------------------------------------------------------------- */
+typedef struct {
+    int32_t objective;   /* NVFP4_MSE or NVFP4_WMSE */
+    int32_t lo, hi;      /* window offsets, -125 <= lo <= 0 <= hi <= 125 unless exhaustive */
+    int32_t exhaustive;  /* nonzero: every code 1..126 */
+    uint8_t* scales;     /* device, uint8 [batch, out, in/16] */
+    uint8_t* packed;     /* device, uint8 [batch, out, in/2], 8-byte aligned */
+    float* loss;         /* device, float [batch, out, in/16], or NULL */
+    int8_t* offset;      /* device, int8 [batch, out, in/16], or NULL */
+} nvfp4_search_rule;
+
+nvfp4_status nvfp4_scale_search_rules(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                      int64_t in, int64_t ldw, int64_t stride_w,
+                                      int32_t group_size, const float* h, int64_t stride_h,
+                                      const float* S, const nvfp4_search_rule* rules,
+                                      int32_t n_rules, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Steps 3-4 with a proposal-centred window and the incoming scale kept on ties ([SR] §4.1.3 and
  * §4.1.4: a proposal gives a neighbourhood of exportable scales that is then scored, and keeping
  * the status-quo scale means the local search cannot increase the loss; [SR] App. D.2: a

@@ -22,7 +22,8 @@ def _declared():
 def test_header_declares_the_boundary():
     names = _declared()
     for want in ("nvfp4_diag_hessian", "nvfp4_diag_hessian_batched", "nvfp4_global_scale",
-                 "nvfp4_scale_search", "nvfp4_scale_search_proposal", "nvfp4_pack",
+                 "nvfp4_scale_search", "nvfp4_scale_search_rules", "nvfp4_scale_search_proposal",
+                 "nvfp4_pack",
                  "nvfp4_output_error", "nvfp4_output_error_workspace_size",
                  "nvfp4_quantize_activations", "nvfp4_quantize_activations_workspace_size",
                  "nvfp4_diag_hessian_finalize", "nvfp4_gptq", "nvfp4_gptq_workspace_size",
@@ -89,6 +90,46 @@ def test_scale_search_rejects_bad_arguments(lib):
     assert _search(lib, inp=0, ldw=0) == n.OK
     # an exhaustive search ignores the window
     assert _search(lib, exh=1, lo=5, hi=-5, W=None) == n.ERR_NULL
+
+
+def _rules(lib, rules=None, n=None, **kw):
+    from block_scale_search_amd import nvfp4 as nv
+    a = dict(W=FAKE, dt=1, batch=1, out=4, inp=64, ldw=64, sw=256, gs=16, h=FAKE, sh=0, S=FAKE)
+    a.update(kw)
+    if rules is None:
+        rules = [dict(objective=0, lo=-3, hi=7), dict(objective=1, lo=-8, hi=7)]
+    arr = (nv.SearchRule * max(1, len(rules)))()
+    for k, r in enumerate(rules):
+        arr[k] = nv.SearchRule(r.get("objective", 1), r.get("lo", -9), r.get("hi", 6),
+                               r.get("exhaustive", 0), r.get("scales", FAKE.value),
+                               r.get("packed", FAKE.value), r.get("loss"), r.get("offset"))
+    return lib.nvfp4_scale_search_rules(a["W"], a["dt"], a["batch"], a["out"], a["inp"], a["ldw"],
+                                        a["sw"], a["gs"], a["h"], a["sh"], a["S"],
+                                        None if n == "null" else arr,
+                                        len(rules) if n in (None, "null") else n, None)
+
+
+def test_scale_search_rules_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    from block_scale_search_amd.nvfp4 import SearchRule
+    lib.nvfp4_scale_search_rules.argtypes = [ctypes.c_void_p, ctypes.c_int] + [ctypes.c_int64] * 5 + [
+        ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+        ctypes.POINTER(SearchRule), ctypes.c_int32, ctypes.c_void_p]
+    assert _rules(lib, gs=8) == n.ERR_ARG
+    assert _rules(lib, n=0) == n.ERR_ARG
+    assert _rules(lib, n=65) == n.ERR_ARG
+    assert _rules(lib, n="null") == n.ERR_NULL
+    assert _rules(lib, rules=[dict(objective=2)]) == n.ERR_ARG
+    assert _rules(lib, rules=[dict(lo=-3, hi=7), dict(lo=1, hi=7)]) == n.ERR_WINDOW
+    assert _rules(lib, rules=[dict(exhaustive=1, lo=5, hi=-5)], W=None) == n.ERR_NULL
+    assert _rules(lib, h=None) == n.ERR_NULL                        # a WMSE rule needs h
+    assert _rules(lib, h=ODD) == n.ERR_ALIGN
+    assert _rules(lib, rules=[dict(objective=1), dict(packed=ODD.value)]) == n.ERR_ALIGN
+    assert _rules(lib, rules=[dict(objective=1), dict(scales=None)]) == n.ERR_NULL
+    assert _rules(lib, dt=3) == n.ERR_DTYPE
+    assert _rules(lib, inp=40, ldw=40) == n.ERR_SHAPE
+    assert _rules(lib, batch=2, sh=8) == n.ERR_SHAPE                # h rows overlap
+    assert _rules(lib, out=0) == n.OK                               # empty: nothing enqueued
 
 
 def _proposal(lib, **kw):
