@@ -222,11 +222,13 @@ def pair_label(modes) -> str:
 
 
 def label_modes(cfg, label: str):
-    """The modes a search label covers ("search:A" or "search:A+B"), else []."""
-    if not label.startswith("search:"):
-        return []
-    parts = label[len("search:"):].split("+")
-    return [m for p in parts for m in cfg.modes if m.label == p]
+    """The modes a search label covers (one mode's "search:A", or the paired call's
+    "search:A+B"), else []."""
+    one = [m for m in cfg.modes if label == f"search:{m.label}"]
+    if one:
+        return one
+    pair = paired_modes(cfg)
+    return pair if pair is not None and label == pair_label(pair) else []
 
 
 def algorithmic_ops(cfg, label: str) -> int:
