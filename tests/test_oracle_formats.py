@@ -134,3 +134,39 @@ def test_e4m3_encode_vs_torch(oracle_mod):
 def test_e4m3_encode_saturates(oracle_mod):
     xs = np.array([448.0, 464.0, 470.0, 1e6, 3e38], dtype=np.float32)
     assert oracle_mod.e4m3_encode(xs).tolist() == [126] * 5
+
+
+def _e2m1_from_bits(x32: np.ndarray) -> np.ndarray:
+    """Third formulation, from the binary32 bit fields: below 1 the E2M1 grid is 0.5 apart, so
+    the index is 2x rounded half-to-even (exact in float64); from 1 up, E2M1 keeps one mantissa
+    bit, so the index is 2 + 2e + the top mantissa bit rounded half-to-even on the other 22
+    bits (a carry moves to the next binade); 7 (the value 6) saturates everything above."""
+    b = x32.view(np.uint32)
+    e = (b >> 23).astype(np.int32) - 127
+    keep = ((b >> 22) & 1).astype(np.int32)
+    rest = b & 0x3FFFFF
+    up = (rest > 0x200000) | ((rest == 0x200000) & (keep == 1))
+    normal = np.minimum(2 + 2 * np.clip(e, 0, 3) + keep + up, 7)
+    small = np.rint(x32.astype(np.float64) * 2.0)
+    return np.where(x32 < 1.0, small, normal).astype(np.uint8)
+
+
+def test_e2m1_every_binary32_in_0_16(oracle_mod):
+    """Every non-negative binary32 below 16 (about 1.1e9 patterns): the oracle's midpoint ladder
+    equals the bit-field formulation; the sign is handled apart (the index uses |x|)."""
+    from concurrent.futures import ThreadPoolExecutor
+    top = int(np.float32(16.0).view(np.uint32))
+    step = 1 << 23
+
+    def check(start):
+        xs = np.arange(start, min(start + step, top), dtype=np.uint32).view(np.float32)
+        got = oracle_mod.e2m1_index(xs)
+        want = _e2m1_from_bits(xs)
+        if np.array_equal(got, want):
+            return None
+        bad = np.nonzero(got != want)[0][:5]
+        return f"mismatch at {xs[bad].tolist()}: {got[bad].tolist()} vs {want[bad].tolist()}"
+
+    with ThreadPoolExecutor(max_workers=4) as pool:
+        errors = [e for e in pool.map(check, range(0, top, step)) if e]
+    assert not errors, errors[0]
