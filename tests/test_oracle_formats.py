@@ -170,3 +170,29 @@ def test_e2m1_every_binary32_in_0_16(oracle_mod):
     with ThreadPoolExecutor(max_workers=4) as pool:
         errors = [e for e in pool.map(check, range(0, top, step)) if e]
     assert not errors, errors[0]
+
+
+def test_e4m3_encode_every_binary32_in_range(oracle_mod):
+    """Every binary32 from 2^-10 (half the smallest subnormal code) up to 464 (half-way from 448
+    to the next step; above it the oracle saturates, torch's conversion does not): the oracle's
+    table scan equals torch's float8_e4m3fn conversion, a library routine, about 1.6e8 patterns;
+    below 2^-10 everything encodes to 0."""
+    from concurrent.futures import ThreadPoolExecutor
+    lo = int(np.float32(2.0 ** -10).view(np.uint32))
+    hi = int(np.float32(464.0).view(np.uint32))
+    step = 1 << 22
+
+    def check(start):
+        xs = np.arange(start, min(start + step, hi), dtype=np.uint32).view(np.float32)
+        got = oracle_mod.e4m3_encode(xs)
+        want = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        if np.array_equal(got, want):
+            return None
+        bad = np.nonzero(got != want)[0][:5]
+        return f"mismatch at {xs[bad].tolist()}: {got[bad].tolist()} vs {want[bad].tolist()}"
+
+    with ThreadPoolExecutor(max_workers=8) as pool:
+        errors = [e for e in pool.map(check, range(lo, hi, step)) if e]
+    assert not errors, errors[0]
+    tiny = np.arange(0, lo, 4099, dtype=np.uint32).view(np.float32)
+    assert (oracle_mod.e4m3_encode(tiny) == 0).all()
