@@ -488,8 +488,9 @@ def main():
                          "codes over the first token chunk, outside the step")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU split is "
-              "described in DESIGN.md and is not launched.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); splitting the rows over GPUs "
+              "(with one all-reduce of h and of the amax) is a design only and is not launched.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
