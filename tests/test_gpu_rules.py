@@ -92,3 +92,14 @@ def test_edge_groups(nv):
     h[:16] = 0.0
     S = nv.global_scale(W, nv.GS_AMAX_448)
     _check(nv, W, h, S, [(0, -3, 7, False), (1, -8, 7, False)], "edges")
+
+
+def test_five_rules_two_pairs_and_clipped_windows(nv):
+    """Five rules: two pairs and a single, on groups whose windows clip at code 1 and at 126."""
+    W, h = _inputs(96, 320, torch.bfloat16, seed=51)
+    W[0, :16] = 1e-30          # base code far below: windows clip at 1
+    W[1, :16] = 2e4            # the tensor maximum: windows clip at 126 (rule 448)
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    rules = [(1, -8, 7, False), (0, -3, 7, False), (1, -9, 6, False), (1, -8, 7, False),
+             (0, -5, 5, False)]
+    _check(nv, W, h, S, rules, "five")
