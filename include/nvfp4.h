@@ -15,7 +15,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every pointer named "device" is GPU memory owned by the caller; the library allocates
- *     nothing and keeps no state between calls. Host pointers are named as such.
+ *     no memory and keeps no data between calls (only, per device, the compute-unit count and
+ *     the occupancy figures it queries once). Host pointers are named as such.
  *   - All device work is enqueued on `stream` (a hipStream_t; NULL = the default stream) and is
  *     asynchronous. Argument errors are detected on the host and returned before anything is
  *     enqueued; a failed kernel launch returns NVFP4_ERR_HIP. Nothing is thrown across the ABI.
