@@ -25,6 +25,13 @@ int elem_size(int dtype) {
 
 nvfp4_status hip_status(hipError_t e) { return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_HIP; }
 
+// Largest element span an operand may cover (rows x leading dimension, matrices x matrix
+// stride): every element offset the kernels form then stays far inside int64.
+constexpr int64_t kMaxSpan = (int64_t)1 << 56;
+bool span_ok(int64_t rows, int64_t ld) {
+    return ld <= kMaxSpan && (rows <= 1 || ld <= kMaxSpan / rows);
+}
+
 // Matrix operand [batch, out, in] with row stride ldw and matrix stride stride_w (elements).
 nvfp4_status check_weights(const void* W, int dtype, int64_t batch, int64_t out, int64_t in,
                            int64_t ldw, int64_t stride_w) {
@@ -33,6 +40,7 @@ nvfp4_status check_weights(const void* W, int dtype, int64_t batch, int64_t out,
     if (batch < 0 || out < 0 || in < 0) return NVFP4_ERR_SHAPE;
     if (in % 16 != 0) return NVFP4_ERR_SHAPE;
     if (ldw < in) return NVFP4_ERR_SHAPE;
+    if (!span_ok(out, ldw) || (batch > 1 && !span_ok(batch, stride_w))) return NVFP4_ERR_SHAPE;
     if (batch > 1 && stride_w < out * ldw) return NVFP4_ERR_SHAPE;
     if (batch > 65535) return NVFP4_ERR_SHAPE;
     if (out * (in / 16) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
@@ -76,7 +84,7 @@ static nvfp4_status diag_hessian_impl(const void* X, int x_dtype, const int64_t*
     const int esz = elem_size(x_dtype);
     if (esz == 0) return NVFP4_ERR_DTYPE;
     if (tokens < 0 || in < 0 || segments < 1) return NVFP4_ERR_SHAPE;
-    if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (in % 8 != 0 || ldx < in || ldx % 8 != 0 || !span_ok(tokens, ldx)) return NVFP4_ERR_SHAPE;
     if (segments > 1 && segments >= ((int64_t)1 << 24)) return NVFP4_ERR_SHAPE;
     if (in == 0) return NVFP4_OK;
     // h_acc == h == NULL on one segment: deferred accumulation into the workspace
@@ -175,8 +183,8 @@ nvfp4_status nvfp4_layer_statistics(const void* X, int x_dtype, int64_t tokens, 
                                     void* stream) {
     if (elem_size(x_dtype) == 0) return NVFP4_ERR_DTYPE;
     if (tokens < 0 || in < 0 || out < 0) return NVFP4_ERR_SHAPE;
-    if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
-    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    if (in % 8 != 0 || ldx < in || ldx % 8 != 0 || !span_ok(tokens, ldx)) return NVFP4_ERR_SHAPE;
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, 0);
     if (st != NVFP4_OK) return st;
     if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
     if (in == 0) return NVFP4_OK;
@@ -325,7 +333,7 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
     if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
     if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
     if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return NVFP4_ERR_WINDOW;
-    nvfp4_status st = check_weights(X, x_dtype, 1, tokens, in, ldx, tokens * ldx);
+    nvfp4_status st = check_weights(X, x_dtype, 1, tokens, in, ldx, 0);
     if (st != NVFP4_OK) return st;
     if (tokens == 0 || in == 0) return NVFP4_OK;
     const bool wmse = objective == NVFP4_WMSE;
@@ -373,7 +381,7 @@ nvfp4_status nvfp4_gptq(const void* W, int w_dtype, int64_t out, int64_t in, int
                         void* workspace, size_t workspace_bytes, void* stream) {
     if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
     if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return NVFP4_ERR_WINDOW;
-    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, 0);
     if (st != NVFP4_OK) return st;
     if (out * in >= ((int64_t)1 << 39)) return NVFP4_ERR_SHAPE;
     if ((out + 31) / 32 > 65535) return NVFP4_ERR_SHAPE;   // row tiles of the update grid
@@ -404,9 +412,9 @@ nvfp4_status nvfp4_output_error(const void* X, int x_dtype, int64_t tokens, int6
                                 double* err, int accumulate, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     if (x_dtype != NVFP4_DTYPE_BF16) return NVFP4_ERR_DTYPE;
-    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, out * ldw);
+    nvfp4_status st = check_weights(W, w_dtype, 1, out, in, ldw, 0);
     if (st != NVFP4_OK) return st;
-    if (tokens < 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (tokens < 0 || ldx < in || ldx % 8 != 0 || !span_ok(tokens, ldx)) return NVFP4_ERR_SHAPE;
     if (nvfp4::output_error_tiles(tokens, out) >= ((int64_t)1 << 31)) return NVFP4_ERR_SHAPE;
     if (out == 0) return NVFP4_OK;
     if (err == nullptr) return NVFP4_ERR_NULL;

@@ -21,7 +21,9 @@
  *     asynchronous. Argument errors are detected on the host and returned before anything is
  *     enqueued; a failed kernel launch returns NVFP4_ERR_HIP. Nothing is thrown across the ABI.
  *   - Matrices are row-major. Sizes and leading dimensions are in elements. A matrix argument
- *     with a zero dimension is valid and enqueues no work (except where noted).
+ *     with a zero dimension is valid and enqueues no work (except where noted). Rows times
+ *     leading dimension, and matrices times matrix stride, must each stay within 2^56 elements
+ *     (else NVFP4_ERR_SHAPE).
  *   - Inputs must be finite; results for non-finite inputs are unspecified.
  *   - Results are deterministic: identical inputs give byte-identical outputs (no float atomics).
  *   - Calls that overlap on the same output buffers race; the library does not serialise them.

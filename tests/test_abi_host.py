@@ -84,6 +84,9 @@ def test_scale_search_rejects_bad_arguments(lib):
     assert _search(lib, ldw=68) == n.ERR_ALIGN                    # bf16 rows of 136 bytes
     assert _search(lib, batch=2, sw=100) == n.ERR_SHAPE           # matrices overlap
     assert _search(lib, out=1 << 26, inp=1 << 10, ldw=1 << 10) == n.ERR_SHAPE
+    assert _search(lib, ldw=1 << 62) == n.ERR_SHAPE               # rows x ldw beyond 2^56
+    assert _search(lib, out=1 << 20, ldw=1 << 40) == n.ERR_SHAPE
+    assert _search(lib, batch=2, sw=1 << 60) == n.ERR_SHAPE       # matrices x stride beyond 2^56
     # empty problems are valid and enqueue nothing
     assert _search(lib, out=0) == n.OK
     assert _search(lib, batch=0) == n.OK
@@ -176,6 +179,8 @@ def test_output_error_rejects_bad_arguments(lib):
     assert call(ldx=60) == n.ERR_SHAPE                            # ldx < in
     assert call(T=-1) == n.ERR_SHAPE
     assert call(T=1 << 40, out=1 << 20, ldw=64) == n.ERR_SHAPE   # tile count >= 2^31
+    assert call(T=1 << 20, ldx=1 << 40) == n.ERR_SHAPE           # tokens x ldx beyond 2^56
+    assert call(ldw=1 << 60) == n.ERR_SHAPE
     assert call(err=None) == n.ERR_NULL
     assert call(pk=None) == n.ERR_NULL
     assert call(X=ODD) == n.ERR_ALIGN
@@ -266,6 +271,7 @@ def test_diag_hessian_rejects_bad_arguments(lib):
     H = lib.nvfp4_diag_hessian
     assert H(FAKE, 1, 1000, 60, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_SHAPE    # in % 8
     assert H(FAKE, 1, 1000, 64, 60, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_SHAPE    # ldx < in
+    assert H(FAKE, 1, 1000, 64, 1 << 50, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_SHAPE  # span
     assert H(FAKE, 4, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_DTYPE
     assert H(None, 1, 1000, 64, 64, FAKE, FAKE, 0, FAKE, ws, None) == n.ERR_NULL
     assert H(FAKE, 1, 1000, 64, 64, None, FAKE, 0, FAKE, ws, None) == n.ERR_NULL
@@ -297,6 +303,8 @@ def test_layer_statistics_rejects_bad_arguments(lib):
     assert call(wd=4) == n.ERR_DTYPE
     assert call(inp=40, ldx=40, ldw=40) == n.ERR_SHAPE                    # W's in % 16
     assert call(ldx=60) == n.ERR_SHAPE
+    assert call(ldx=1 << 50) == n.ERR_SHAPE                               # tokens x ldx span
+    assert call(ldw=1 << 60) == n.ERR_SHAPE
     assert call(rule=2) == n.ERR_ARG
     assert call(acc=None) == n.ERR_NULL
     assert call(S=None) == n.ERR_NULL
