@@ -87,6 +87,12 @@ __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)
     L_hi = quad_tree(Q);
 }
 
+// Sequence point between candidates: an empty asm that reads and rewrites v, so everything that
+// produced v is done before it and everything that uses v comes after it. Without it the compiler
+// interleaves the arithmetic of several candidates, which raises the register count and lowers
+// the number of waves a SIMD holds.
+__device__ __forceinline__ void order_point(float& v) { asm volatile("" : "+v"(v)); }
+
 // Running minimum over candidates visited in ascending code order: a strictly smaller loss
 // replaces the best, so the first (lowest) code wins ties.
 __device__ __forceinline__ void keep_min(float L, int c, float& best, int& best_c) {
@@ -111,7 +117,9 @@ __device__ __forceinline__ void scan_block(const float (&w)[16], const float (&h
 #pragma unroll
     for (int p = 0; p < (NB > 0 ? (NB < 8 ? NB : 8) : 8); ++p) {
         if (NB == 0 && p >= n) break;
-        const float2 er = t0[p];
+        float2 er = t0[p];
+        order_point(er.x);
+        order_point(er.y);
         if (p + 8 < n) {
             float L_lo, L_hi;
             loss_pair<WMSE>(w, h, er.x, er.y, t0[p + 8].x, L_lo, L_hi);
@@ -121,6 +129,8 @@ __device__ __forceinline__ void scan_block(const float (&w)[16], const float (&h
             const float L = loss_one<WMSE>(w, h, er.x, er.y);
             if (L < bl) { bl = L; pl = p; }
         }
+        order_point(bl);
+        order_point(bh);
     }
     keep_min(bl, c0 + pl, best, best_c);
     keep_min(bh, c0 + ph, best, best_c);
@@ -152,8 +162,11 @@ __device__ __forceinline__ void search_window(const float (&w)[16], const float 
     for (int p = 0; p < n; ++p) {
         const int c = first + p;
         if (live && c >= 1 && c <= 126) {
-            const float2 er = tab[c];
+            float2 er = tab[c];
+            order_point(er.x);
+            order_point(er.y);
             keep_min(loss_one<WMSE>(w, h, er.x, er.y), c, best, best_c);
+            order_point(best);
         }
     }
 }
@@ -207,9 +220,12 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
     for (int p = 0; p < 8; ++p) {
         const int c = c0 + p;
         const bool in = c >= 1 && c <= 126;
-        const float2 er = tab[in ? c : 1];
+        float2 er = tab[in ? c : 1];
+        order_point(er.x);
+        order_point(er.y);
         const float L = loss_one<WMSE>(w, h, er.x, er.y);
         if (in) keep_min_lex(L, c, best, best_c);
+        order_point(best);
     }
 }
 
