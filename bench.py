@@ -7,9 +7,14 @@ One step = the whole path over one synthetic layer held in HBM:
   for both (--separate-searches times one nvfp4_scale_search call per mode).
 On workloads of one matrix and one token chunk, h and S come from one call
 (nvfp4_layer_statistics, two launches; --separate-stats times the two separate calls).
-With --streams 2 the h-reduce runs on a second stream (same default priority), overlapping the
-global scale and the searches that do not read h; the searches that read h wait for it. The
-default is one stream, so that every kernel's time is its own.
+Steps follow one another as the layers of a model would (--schedule pipeline, the default when
+two or more input sets rotate): step i + 1's h and S calls (HBM-bound) run on a second stream
+while step i's searches (VALU-bound) run on the main stream; every step still does all of its
+work, and a set's next h and S wait for the searches that read the set's previous ones. With
+--schedule sequential every call of a step runs on one stream, in order, so that every kernel's
+time is its own. With --streams 2 (sequential across steps) the h-reduce runs on a second
+stream, overlapping the global scale and the searches that do not read h. All streams keep the
+default priority.
 After the timed steps, the pack-at-given-scales entry point (not part of a step) is timed on
 its own over the same layers, with the scale bytes the last search wrote.
 Prints one JSON line. `value` is weight-searches per second: every mode run searches each of the
@@ -131,17 +136,21 @@ class Runner:
                 s.incoming = base.contiguous()
             torch.cuda.synchronize()
 
-    def calls(self, s: Layer, aux=None):
+    def calls(self, s: Layer, aux=None, stage=None):
         """The step as (label, call, stream_role) triples in issue order; each call is a prepared
         C-ABI invocation (arguments marshalled once). With an auxiliary stream, the h-reduce
         runs there ("aux") while the main stream computes the global scale and the searches
-        that do not read h; the searches that read h wait for it ("main_after_h")."""
+        that do not read h; the searches that read h wait for it ("main_after_h"). With a
+        stage stream, every call that produces h and S runs there ("stage") and the searches
+        run on the main stream."""
         nv, cfg = self.nv, self.cfg
         b, o, n = cfg.batch, cfg.out, cfg.inp
         ldw, sw = n, o * n
         out = []
         import torch
-        hs = aux if aux is not None else torch.cuda.current_stream()
+        hs = aux if aux is not None else (stage if stage is not None else
+                                          torch.cuda.current_stream())
+        h_role = "stage" if stage is not None else "aux"
         deferred = len(s.chunks) > 1 and s.seg is None
         # one matrix, one token chunk, one stream: h and S in one call (two launches)
         fused = aux is None and s.seg is None and len(s.chunks) == 1 and not self.separate_stats
@@ -149,30 +158,31 @@ class Runner:
             X = s.chunks[0]
             out.append(("h_reduce+global_scale", nv.nvfp4_layer_statistics(
                 X, X.shape[0], n, n, s.h_acc, s.h, False, s.W, o, ldw, self.rule, s.S,
-                self.ws_ls, prepare=True), "main"))
+                self.ws_ls, stream=stage, prepare=True), "stage" if stage is not None else "main"))
         for ci, X in enumerate(s.chunks if not fused else []):
             T = X.shape[0]
             if s.seg is not None:
                 out.append(("h_reduce", nv.nvfp4_diag_hessian_batched(
                     X, s.seg, b, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, stream=hs,
-                    prepare=True), "aux"))
+                    prepare=True), h_role))
             elif deferred:
                 # token chunks of one calibration set: row-group sums accumulate in the
                 # workspace, one finalize after the last chunk
                 out.append(("h_reduce", nv.nvfp4_diag_hessian(
                     X, T, n, n, None, None, ci > 0, self.ws_h, stream=hs, prepare=True),
-                    "aux"))
+                    h_role))
             else:
                 out.append(("h_reduce", nv.nvfp4_diag_hessian(
                     X, T, n, n, s.h_acc, s.h, ci > 0, self.ws_h, stream=hs, prepare=True),
-                    "aux"))
+                    h_role))
         if deferred:
             out.append(("h_finalize", nv.nvfp4_diag_hessian_finalize(
                 s.chunks[0].dtype, s.chunks[0].shape[0], n, s.h_acc, s.h, False, self.ws_h,
-                stream=hs, prepare=True), "aux"))
+                stream=hs, prepare=True), h_role))
         if not fused:
             out.append(("global_scale", nv.nvfp4_global_scale(
-                s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, prepare=True), "main"))
+                s.W, b, o, n, ldw, sw, self.rule, s.S, self.ws_s, stream=stage, prepare=True),
+                "stage" if stage is not None else "main"))
         pair = None if self.separate_searches else paired_modes(cfg)
         if pair is not None:
             # two windowed rules in one call: one launch reads each group once for both
@@ -200,7 +210,7 @@ class Runner:
                 nv.WMSE if wm else nv.MSE, m.lo, m.hi, m.exhaustive, s.S, s.scales[mi],
                 s.packed[mi], prepare=True), "main_after_h" if wm else "main"))
         # issue order: aux work first, then main work that does not need h, then the rest
-        rank = {"aux": 0, "main": 1, "main_after_h": 2}
+        rank = {"aux": 0, "stage": 0, "main": 1, "main_after_h": 2}
         return sorted(out, key=lambda t: rank[t[2]])
 
 
@@ -472,6 +482,10 @@ def main():
     ap.add_argument("--streams", type=int, default=1, choices=(1, 2),
                     help="2: h-reduce on a second stream, overlapping the global scale and the "
                          "searches that do not read h")
+    ap.add_argument("--schedule", default="pipeline", choices=("pipeline", "sequential"),
+                    help="pipeline: the next step's h and S calls run on a second stream while "
+                         "this step's searches run (needs two or more input sets and one "
+                         "stream); sequential: every call of a step on one stream, in order")
     ap.add_argument("--events-every", type=int, default=8,
                     help="record per-call HIP events on every Nth timed step (1 = all)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -517,7 +531,25 @@ def main():
 
     main = torch.cuda.current_stream()
     aux = torch.cuda.Stream() if args.streams == 2 else None
-    steps = [runner.calls(s, aux) for s in runner.sets]
+    # Layer pipeline: step i + 1's h and S (HBM-bound) run on the stage stream while step i's
+    # searches (VALU-bound) run on the main stream. Each input set has its own h, S and outputs;
+    # a set's next h and S wait for the searches of its previous use, so two or more sets are
+    # needed. Both streams keep the default priority.
+    pipelined = args.schedule == "pipeline" and aux is None and n_sets >= 2
+    schedule = "pipeline" if pipelined else "sequential"
+    stage = torch.cuda.Stream() if pipelined else None
+    steps = [runner.calls(s, aux, stage) for s in runner.sets]
+
+    def timed_call(f, st, timed_row):
+        if timed_row is None:
+            f()
+            return
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        f()
+        e1.record(st)
+        timed_row.append((e0, e1))
 
     def run_step(calls, timed_row=None):
         """One step. Two streams: the aux stream starts when the step starts (event), the
@@ -530,20 +562,48 @@ def main():
             if aux is not None and role == "main_after_h" and not waited:
                 main.wait_stream(aux)
                 waited = True
-            if timed_row is None:
-                f()
-                continue
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(st)
-            f()
-            e1.record(st)
-            timed_row.append((e0, e1))
+            timed_call(f, st, timed_row)
         if aux is not None and not waited:
             main.wait_stream(aux)
 
-    for i in range(args.warmup):
-        run_step(steps[i % n_sets])
+    ev_stage = [torch.cuda.Event() for _ in range(n_sets)]
+    ev_done = [torch.cuda.Event() for _ in range(n_sets)]
+
+    def run_pipelined(first, count, rows=None):
+        """Steps first .. first + count - 1 of the set rotation, pipelined. rows (a dict) receives
+        each timed step's (start, end) event pairs in call order."""
+        def want(i):
+            return rows is not None and (i - first) % args.events_every == 0
+
+        def issue_stage(i):
+            k = i % n_sets
+            if i - first >= n_sets:
+                stage.wait_event(ev_done[k])          # the set's previous searches are done
+            row = rows.setdefault(i, []) if want(i) else None
+            for lab, f, role in steps[k]:
+                if role == "stage":
+                    timed_call(f, stage, row)
+            ev_stage[k].record(stage)
+
+        stage.wait_stream(main)
+        issue_stage(first)
+        for i in range(first, first + count):
+            k = i % n_sets
+            if i + 1 < first + count:
+                issue_stage(i + 1)
+            main.wait_event(ev_stage[k])
+            row = rows.setdefault(i, []) if want(i) else None
+            for lab, f, role in steps[k]:
+                if role != "stage":
+                    timed_call(f, main, row)
+            ev_done[k].record(main)
+        main.wait_stream(stage)
+
+    if pipelined:
+        run_pipelined(0, args.warmup)
+    else:
+        for i in range(args.warmup):
+            run_step(steps[i % n_sets])
     torch.cuda.synchronize()
 
     labels = [lab for lab, _, _ in steps[0]]
@@ -552,13 +612,18 @@ def main():
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_start.record(main)
-    for i in range(args.steps):
-        if i % args.events_every:
-            run_step(steps[i % n_sets])
-            continue
-        row = []
-        run_step(steps[i % n_sets], row)
-        ev.append(row)
+    if pipelined:
+        rows = {}
+        run_pipelined(args.warmup, args.steps, rows)
+        ev = [rows[i] for i in sorted(rows)]
+    else:
+        for i in range(args.steps):
+            if i % args.events_every:
+                run_step(steps[i % n_sets])
+                continue
+            row = []
+            run_step(steps[i % n_sets], row)
+            ev.append(row)
     t_end.record(main)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -849,7 +914,7 @@ def main():
         "config": {"workload": cfg.description, "name": cfg.name,
                    "modes": [m.label for m in cfg.modes], "global_scale": cfg.gs_rule,
                    "weights_per_step": searched, "input_sets_rotated": n_sets,
-                   "streams": args.streams},
+                   "streams": args.streams, "schedule": schedule},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,
