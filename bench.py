@@ -514,7 +514,10 @@ def main():
     dev = torch.device("cuda:0")
     per_set = cfg.n_weights * (2 if str(cfg.w_dtype).endswith("bfloat16") else 4) + \
         cfg.tokens * cfg.inp * 2
-    n_sets = args.sets or max(1, min(8, -(-(1 << 30) // per_set)))
+    # enough sets for more than 1 GiB of inputs (past the 256 MB MALL), at most 8; the layer
+    # pipeline needs at least two
+    n_sets = args.sets or max(2 if args.schedule == "pipeline" else 1,
+                              min(8, -(-(1 << 30) // per_set)))
     print(f"# workload {cfg.name}: {cfg.description}; {n_sets} input set(s)", file=sys.stderr,
           flush=True)
     runner = Runner(cfg, n_sets, dev)
