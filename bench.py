@@ -671,6 +671,21 @@ def main():
         torch.cuda.synchronize()
         h_alone_us = p0.elapsed_time(p1) * 1e3 / reps_h
 
+    # under the layer pipeline the searches share the chip with the next step's h and S; each
+    # search call is also timed alone (back to back over the sets, outside the step), which gives
+    # the kernel's own rate beside the roofline entry of the timed steps
+    search_alone = {}
+    if pipelined:
+        for lab in dict.fromkeys(l for l in labels if l.startswith("search")):
+            fs = [f for st_ in steps for l, f, r in st_ if l == lab]
+            reps_s = 10 * len(fs)
+            p0.record(main)
+            for i in range(reps_s):
+                fs[i % len(fs)]()
+            p1.record(main)
+            torch.cuda.synchronize()
+            search_alone[lab] = p0.elapsed_time(p1) * 1e3 / reps_s
+
     # layer-output error (evaluation, outside the step): X chunk 0 against W and the last
     # mode's codes of each input set
     oe = None
@@ -872,6 +887,13 @@ def main():
                 "alg_bytes_per_launch": nb, "alg_flops_per_launch": nf,
                 "hbm_GB/s_algorithmic": kernels[dom]["GB/s"],
                 "hbm_frac_algorithmic": kernels[dom]["frac_hbm"]}
+    if dom in search_alone:
+        ua = search_alone[dom]
+        roofline["alone"] = {
+            "avg_us": round(ua, 3), "achieved": round(no / ua / 1e6, 2),
+            "frac": round(no / ua / 1e6 / VALU_PEAK_TOPS, 4),
+            "note": "the same call back to back outside the timed steps; in the steps it shares "
+                    "the compute units with the next step's h and S"}
 
     cpu = None
     if not args.no_cpu:
