@@ -501,6 +501,8 @@ def main():
                     help="also time the layer-output error evaluation (MFMA) of the last mode's "
                          "codes over the first token chunk, outside the step")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.events_every < 1:
+        ap.error("--steps and --events-every must be at least 1, --warmup at least 0")
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); splitting the rows over GPUs "
               "(with one all-reduce of h and of the amax) is a design only and is not launched.",
@@ -588,6 +590,8 @@ def main():
                     timed_call(f, stage, row)
             ev_stage[k].record(stage)
 
+        if count <= 0:
+            return
         stage.wait_stream(main)
         issue_stage(first)
         for i in range(first, first + count):
