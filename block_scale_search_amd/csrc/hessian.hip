@@ -51,13 +51,15 @@ struct XCols {
 };
 
 // Row groups: segment e has groups [group_prefix[e], group_prefix[e+1]); one segment without
-// an offsets array has groups [0, ceil(tokens / rows_per_group)).
+// an offsets array has groups [0, single_groups). The kernels only need the group count: the
+// groups of a segment take its V-row blocks round-robin, which works for any count >= 1.
 struct GroupMap {
     const int64_t* seg_offsets;  // NULL: one segment [0, tokens)
     const int32_t* group_prefix;
     int64_t segments;
     int64_t tokens;
-    int64_t rows_per_group;
+    int64_t rows_per_group;      // several segments: rows per group of every segment
+    int64_t single_groups;       // one segment: its group count
 };
 
 __host__ __device__ __forceinline__ int64_t groups_for(int64_t rows, int64_t rows_per_group) {
@@ -69,7 +71,7 @@ __device__ __forceinline__ bool map_group(const GroupMap& m, int64_t grp, int64_
                                           int64_t& row0, int64_t& row1, int64_t& g,
                                           int64_t& count) {
     if (m.seg_offsets == nullptr) {
-        count = groups_for(m.tokens, m.rows_per_group);
+        count = m.single_groups;
         if (grp >= count) return false;
         e = 0;
         g = grp;
@@ -212,7 +214,7 @@ __device__ __forceinline__ void hess_finalize_body(const double* __restrict__ pa
                                                    double (*red)[kFinCols]) {
     const int cl = threadIdx.x % kFinCols, sub = threadIdx.x / kFinCols;
     const int64_t c = blk * kFinCols + cl;
-    int64_t first = 0, count = groups_for(map.tokens, map.rows_per_group);
+    int64_t first = 0, count = map.single_groups;
     if (map.seg_offsets != nullptr) {
         first = map.group_prefix[e];
         count = map.group_prefix[e + 1] - first;
@@ -294,11 +296,23 @@ int64_t strips_for(int64_t in, bool bf16) {
     return (in + sw - 1) / sw;
 }
 
-// Rows per row group: enough groups for about kTargetGroups workgroups over all strips.
+// Several segments: rows per row group of every segment, enough groups for about
+// kTargetGroups workgroups over all strips and all segments' tokens.
 int64_t rows_per_group(int64_t tokens, int64_t in, bool bf16) {
     const int64_t want = (tokens * strips_for(in, bf16) + kTargetGroups - 1) / kTargetGroups;
     const int64_t r = want < 16 ? 16 : want;
     return (r + 7) / 8 * 8;
+}
+
+// One segment: one row group per 16 rows, at most enough for about kTargetGroups workgroups
+// over all strips. The count never decreases as tokens grow, so in a deferred sequence whose
+// first chunk is the longest every later chunk writes only slots the first one initialised,
+// and the finalize (given the first chunk's token count) sums every slot that holds data.
+int64_t single_groups(int64_t tokens, int64_t in, bool bf16) {
+    if (tokens <= 0) return 0;
+    const int64_t cap = (kTargetGroups + strips_for(in, bf16) - 1) / strips_for(in, bf16);
+    const int64_t g = (tokens + 15) / 16;
+    return g < cap ? g : (cap > 0 ? cap : 1);
 }
 
 size_t prefix_bytes(int64_t segments) {
@@ -306,8 +320,8 @@ size_t prefix_bytes(int64_t segments) {
 }
 
 int64_t max_groups(int64_t tokens, int64_t in, int64_t segments, bool bf16) {
-    const int64_t g = groups_for(tokens, rows_per_group(tokens, in, bf16));
-    return segments > 1 ? g + segments : g;
+    if (segments <= 1) return single_groups(tokens, in, bf16);
+    return groups_for(tokens, rows_per_group(tokens, in, bf16)) + segments;
 }
 
 }  // namespace
@@ -331,7 +345,7 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
     const bool batched = seg_offsets != nullptr;
     const int64_t E = batched ? segments : 1;
     GroupMap map{batched ? seg_offsets : nullptr, nullptr, E, tokens,
-                 rows_per_group(tokens, in, bf16)};
+                 rows_per_group(tokens, in, bf16), single_groups(tokens, in, bf16)};
     // workspace: [group prefix (batched only) | row-group partials]
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     if (batched) {
@@ -378,7 +392,8 @@ hipError_t launch_layer_statistics(const void* X, bool x_bf16, int64_t tokens, i
                                    int64_t ldx, double* h_acc, float* h, bool accumulate,
                                    const void* W, bool w_bf16, int64_t out, int64_t ldw, int rule,
                                    float* S, void* workspace, hipStream_t stream) {
-    GroupMap map{nullptr, nullptr, 1, tokens, rows_per_group(tokens, in, x_bf16)};
+    GroupMap map{nullptr, nullptr, 1, tokens, rows_per_group(tokens, in, x_bf16),
+                 single_groups(tokens, in, x_bf16)};
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     double* partial = reinterpret_cast<double*>(ws);
     uint32_t* amax_partial =

@@ -90,7 +90,10 @@ const char* nvfp4_version(void);
  * accumulate == 0), and nvfp4_diag_hessian_finalize later turns the workspace into h_acc and
  * h. One finalize per set instead of one per chunk. Every call of a sequence uses the same
  * workspace, x_dtype and in; the first call has accumulate == 0 and the largest token count
- * of the sequence, which finalize is given as `tokens` (it fixes the workspace layout).
+ * of the sequence, which finalize is given as `tokens` (it fixes the workspace layout). The
+ * number of workspace slots a call writes never decreases as its token count grows, so every
+ * later, shorter chunk adds only into slots that the first call initialised. A later chunk
+ * longer than the first is outside this contract: its extra slots are not summed.
  * ------------------------------------------------------------------------------------------- */
 size_t nvfp4_diag_hessian_workspace_size(int64_t tokens, int64_t in, int64_t segments);
 

@@ -314,3 +314,16 @@ def test_layer_statistics_rejects_bad_arguments(lib):
     assert call(wsb=ws - 1) == n.ERR_WORKSPACE
     assert call(ws=None) == n.ERR_WORKSPACE
     assert call(inp=0, ldx=0, ldw=0, X=None, acc=None, W=None, S=None, ws=None, wsb=0) == n.OK
+
+
+def test_deferred_hessian_slots_never_shrink_with_tokens(lib):
+    """A deferred h sequence writes its chunks' row-group sums into workspace slots laid out by
+    the first (longest) chunk. A shorter later chunk must use no slot that the first one did not
+    initialise, so the slot count of one segment may not decrease as the token count grows.
+    The single-segment workspace is slots x in x 8 bytes, so its size shows the count."""
+    for inp in (8, 136, 512, 1040, 4096, 8192, 14336, 28672):
+        sizes = [lib.nvfp4_diag_hessian_workspace_size(t, inp, 1) for t in range(0, 20001)]
+        for t in range(1, len(sizes)):
+            assert sizes[t] >= sizes[t - 1], (inp, t)
+        # the shapes the advisor found out of order: 1025 vs 1024 and 7936 vs 7680 tokens
+        assert sizes[1025] >= sizes[1024] and sizes[7936] >= sizes[7680]

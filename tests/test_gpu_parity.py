@@ -387,3 +387,31 @@ def test_hessian_deferred_chunks(nv, dtype):
     nv.nvfp4_diag_hessian_finalize(dtype, T0, inp, h_acc, None, True, ws)
     torch.cuda.synchronize()
     np.testing.assert_allclose(h_acc.cpu().numpy(), 2 * acc_o, rtol=1e-12, atol=0)
+
+
+@pytest.mark.parametrize("inp,sizes,ws_tokens", [
+    (4096, [1025, 1024], 8192),               # workspace larger than the first chunk needs
+    (4096, [7936, 7680, 1025, 17, 1], 7936),
+    (1040, [3000, 16, 3000, 1], 3000),
+])
+def test_hessian_deferred_ragged_chunks(nv, inp, sizes, ws_tokens):
+    """Deferred mode with chunks of falling and ragged sizes (the first the longest), some
+    with fewer row-group slots than the first: every token lands in a slot the first chunk
+    initialised, so the finalize over the first chunk's layout equals the oracle over all
+    tokens."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(sum(sizes) + inp)
+    chunks = [(torch.randn((t, inp), generator=g, device=DEV) *
+               torch.exp(torch.randn(inp, generator=g, device=DEV))).to(torch.bfloat16)
+              for t in sizes]
+    ws = torch.empty(nv.nvfp4_diag_hessian_workspace_size(ws_tokens, inp, 1), dtype=torch.uint8,
+                     device=DEV)
+    for i, X in enumerate(chunks):
+        nv.nvfp4_diag_hessian(X, X.shape[0], inp, inp, None, None, i > 0, ws)
+    h_acc = torch.empty(inp, dtype=torch.float64, device=DEV)
+    h = torch.empty(inp, dtype=torch.float32, device=DEV)
+    nv.nvfp4_diag_hessian_finalize(torch.bfloat16, sizes[0], inp, h_acc, h, False, ws)
+    torch.cuda.synchronize()
+    acc_o, h_o = oracle.diag_hessian(host_w(torch.cat(chunks)))
+    np.testing.assert_allclose(h_acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
