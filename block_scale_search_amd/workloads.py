@@ -178,6 +178,17 @@ CONFIGS = {
 }
 
 
+# Workloads of several matrices measured as one step: the 70B-shaped MLP pair, the up/gate
+# projection (28672x8192, X 65536x8192) and the down projection (8192x28672, X 65536x28672),
+# each streamed in 8192-token chunks and searched in both of its modes.
+GROUPS = {"mlp70b": ("mlp70b_up", "mlp70b_down")}
+
+
+def workload_configs(name: str) -> list:
+    """The configs a named workload covers: one, or every matrix of a group."""
+    return [CONFIGS[n] for n in GROUPS.get(name, (name,))]
+
+
 def proposal_offsets(cfg: Config, shape, device="cpu"):
     """Seeded integer offsets in [-3, 3] that move a group's base code to a synthetic proposal
     (the pages' proposals come from a GPTQ-state quadratic fit that needs trained weights)."""
