@@ -1,7 +1,8 @@
 // Device-side pieces of the global-scale reduction for gfx950, shared by the global-scale
 // kernels and the fused layer-statistics kernels: max |w| on binary32 bit patterns (exact and
 // independent of the reduction order) and the scale rule S = amax / 2688 or amax / 1536, 1 for
-// amax = 0 (H-Scale §3: tensor-wide FP32 scale; ScaleSweep §3: the 256 * 6 adjustment).
+// amax = 0 (H-Scale §3: tensor-wide FP32 scale; ScaleSweep Methodology §2: the 256 * 6
+// adjustment).
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -1,7 +1,7 @@
 // Global FP32 scale of a weight matrix (or of each matrix of a batch) for gfx950:
 // S = amax / 2688 (448 * 6) or S = amax / 1536 (256 * 6), and S = 1 when amax = 0
 // (H-Scale §3: the tensor-wide FP32 scale times the per-group E4M3 scale gives the effective
-// scale; ScaleSweep §3: the 256 * 6 adjustment of the per-tensor rule).
+// scale; ScaleSweep Methodology §2: the 256 * 6 adjustment of the per-tensor rule).
 //
 // max |w| is taken on the binary32 bit patterns of non-negative values, which order like
 // unsigned integers, so the result is exact and independent of the reduction order.
