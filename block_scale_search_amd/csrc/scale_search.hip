@@ -92,7 +92,7 @@ template <bool BF16, bool WMSE, int NWIN, bool PROPOSAL, bool SFP>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
     uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec, int64_t stride_h,
-    int lo, int hi, int exhaustive, ScaleSource src, uint8_t* __restrict__ scales,
+    int lo, int hi, ScaleSource src, uint8_t* __restrict__ scales,
     uint8_t* __restrict__ packed, float* __restrict__ loss_out, int8_t* __restrict__ off_out,
     const uint8_t* __restrict__ center, const uint8_t* __restrict__ incoming) {
     __shared__ float2 tab[128];
@@ -138,12 +138,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     // The running best starts at +inf with the first candidate's code, so a group whose every
     // loss overflows keeps its first candidate, as the ascending scan does.
     float best = __builtin_inff();
-    int best_c = exhaustive ? 1 : min(max(cen + lo, 1), 126);
-    if (exhaustive) {
-        if (__any(live)) search_all<WMSE>(w, h, tab, octave_ok, live, b, best, best_c);
-    } else {
-        search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, cen + lo, hi - lo + 1, best, best_c);
-    }
+    int best_c = min(max(cen + lo, 1), 126);
+    search_window<WMSE, NWIN>(w, h, tab, octave_ok, live, cen + lo, hi - lo + 1, best, best_c);
     if constexpr (PROPOSAL) {
         // the incoming code comes first in the scan order, so it wins every tie
         if (live && inc >= 1 && inc <= 126) {
@@ -163,6 +159,108 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
     if (valid)
         emit_group(w, tab, best_c, best, live ? best_c - cen : 0, gidx,
                    RuleOut{scales, packed, loss_out, off_out});
+}
+
+// Exhaustive mode (every code 1..126): the three phases of search_device.h's exhaustive search.
+// Phase 1 per lane (centre block, pending block counts), phase 2 the wave's pending 8-code
+// blocks dealt over its lanes, phase 3 each lane's result from its LDS slot, then the output.
+// The weights and h of a group are read again where phase 2 or the output needs them instead of
+// being held in registers through the kernel, which keeps the register count (and the waves per
+// SIMD) of the windowed kernel.
+template <bool BF16, bool WMSE>
+__global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
+    uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec,
+    int64_t stride_h, const float* __restrict__ S_arr, RuleOut o) {
+    __shared__ float2 tab[128];
+    __shared__ int flag;
+    __shared__ int first_item[kSearchThreads];             // per wave: exclusive prefix of counts
+    __shared__ unsigned long long slot[kSearchThreads];    // per lane: min (loss, code) key
+    const int64_t batch = blockIdx.y;
+    const uint32_t gpr = in >> 4;
+    const uint32_t G = out * gpr;
+    const uint32_t wave0 = threadIdx.x & ~63u;
+    const int lane = threadIdx.x & 63;
+    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
+    const bool valid = gi < G;
+    const uint8_t* Wm = W + batch * stride_w_bytes;
+    const float* hm = hvec + batch * stride_h;
+    const float S = S_arr[batch];
+
+    // phase 1
+    int b, c0 = 8, n_up = 0, n_dn = 0;
+    bool live;
+    {
+        const uint32_t row = valid ? div_gpr(gi, gpr_magic, gpr_shift) : 0u;
+        const uint32_t g = valid ? gi - row * gpr : 0u;
+        float w[16], h[16];
+        load_inputs<BF16, WMSE>(Wm, ldw_bytes, hm, valid, row, g, w, h);
+        const bool octave_ok = build_table(S, tab, &flag);
+        b = base_code(w, S);
+        live = valid && b > 0;
+        // +inf with code 1: a group whose every loss overflows keeps code 1, as the ascending
+        // scan does
+        float best = __builtin_inff();
+        int best_c = 1;
+        if (__any(live))
+            exhaustive_centre<WMSE>(w, h, tab, octave_ok, live, b, best, best_c, c0, n_up, n_dn);
+        slot[threadIdx.x] = loss_key(best, best_c);
+    }
+
+    // phase 2: exclusive prefix of the lanes' block counts, then rounds of one block per lane
+    const int n = n_up + n_dn;
+    int incl = n;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int v = __shfl_up(incl, d, 64);
+        if (lane >= d) incl += v;
+    }
+    const int total = __shfl(incl, 63, 64);
+    first_item[threadIdx.x] = incl - n;
+    __syncthreads();
+    for (int t0 = 0; t0 < total; t0 += 64) {
+        const int t = t0 + lane;
+        const bool has = t < total;
+        // owner: the last lane whose first item is <= t (lanes without items share the next
+        // lane's first item and are passed over)
+        int j = 0;
+#pragma unroll
+        for (int step = 32; step >= 1; step >>= 1)
+            if (first_item[wave0 + j + step] <= t) j += step;
+        const int owner = has ? j : lane;
+        const int k = t - first_item[wave0 + owner];
+        const int o_up = __shfl(n_up, owner, 64);
+        const int o_c0 = __shfl(c0, owner, 64);
+        // block k of the owner: upward from o_c0 + 16, then downward from o_c0 - 1
+        const int first = !has ? 8 : (k < o_up ? o_c0 + 16 + 8 * k : o_c0 - 8 * (k - o_up) - 8);
+        const uint32_t ogi = blockIdx.x * kSearchThreads + wave0 + owner;
+        const bool ovalid = has && ogi < G;
+        const uint32_t orow = ovalid ? div_gpr(ogi, gpr_magic, gpr_shift) : 0u;
+        const uint32_t og = ovalid ? ogi - orow * gpr : 0u;
+        float w[16], h[16];
+        load_inputs<BF16, WMSE>(Wm, ldw_bytes, hm, ovalid, orow, og, w, h);
+        float bl = __builtin_inff();
+        int cl = 255;
+        scan8<WMSE>(w, h, tab, first, bl, cl);
+        if (has) atomicMin(&slot[wave0 + owner], (unsigned long long)loss_key(bl, cl));
+    }
+    __syncthreads();
+
+    // phase 3
+    const uint64_t key = slot[threadIdx.x];
+    float best = key_loss(key);
+    int best_c = key_code(key);
+    if (!live) {
+        best = 0.0f;
+        best_c = 0;
+    }
+    if (valid) {
+        const uint32_t row = div_gpr(gi, gpr_magic, gpr_shift);
+        const uint32_t g = gi - row * gpr;
+        float w[16], h[16];
+        load_inputs<BF16, false>(Wm, ldw_bytes, hm, true, row, g, w, h);
+        emit_group(w, tab, best_c, best, live ? best_c - b : 0, batch * (int64_t)G + gi, o);
+    }
 }
 
 // Two windowed rules on one read of each group (bf16 W): the weights, h, S, the code table and
@@ -219,7 +317,7 @@ struct SearchArgs {
     int64_t ldw_bytes, stride_w_bytes;
     const float* h;
     int64_t stride_h;
-    int lo, hi, exhaustive;
+    int lo, hi;
     ScaleSource src;
     uint8_t *scales, *packed;
     float* loss;
@@ -231,7 +329,7 @@ template <bool B, bool M, int N, bool P, bool SFP>
 void launch_one(const SearchArgs& a, dim3 grid, hipStream_t stream) {
     hipLaunchKernelGGL((k_scale_search<B, M, N, P, SFP>), grid, dim3(kSearchThreads), 0, stream,
                        a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes, a.stride_w_bytes, a.h,
-                       a.stride_h, a.lo, a.hi, a.exhaustive, a.src, a.scales, a.packed, a.loss,
+                       a.stride_h, a.lo, a.hi, a.src, a.scales, a.packed, a.loss,
                        a.offset, a.center, a.incoming);
 }
 
@@ -346,7 +444,6 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
     a.stride_h = stride_h;
     a.lo = lo;
     a.hi = hi;
-    a.exhaustive = exhaustive ? 1 : 0;
     a.src = src;
     a.scales = scales;
     a.packed = packed;
@@ -358,7 +455,23 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
     const int n = hi - lo + 1;
     const bool proposal = center != nullptr;
     const bool sfp = src.amax_partial != nullptr;
-    const int nwin = exhaustive ? 0 : (n == 16 || n == 11 || n == 9 ? n : 0);
+    if (exhaustive) {
+        // every code 1..126 around the base code, with S given (no proposal, no fused S)
+        if (proposal || sfp || src.S == nullptr) return hipErrorInvalidValue;
+        const RuleOut o{scales, packed, loss, offset};
+#define NVFP4_EXH(B, M)                                                                        \
+        hipLaunchKernelGGL((k_scale_search_exhaustive<B, M>), grid, dim3(kSearchThreads), 0,   \
+                           stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes,            \
+                           a.stride_w_bytes, a.h, a.stride_h, src.S, o)
+        if (bf16) {
+            if (wmse) NVFP4_EXH(true, true); else NVFP4_EXH(true, false);
+        } else {
+            if (wmse) NVFP4_EXH(false, true); else NVFP4_EXH(false, false);
+        }
+#undef NVFP4_EXH
+        return hipGetLastError();
+    }
+    const int nwin = n == 16 || n == 11 || n == 9 ? n : 0;
     if (bf16) {
         if (wmse) launch_modes<true, true>(a, nwin, proposal, sfp, grid, stream);
         else launch_modes<true, false>(a, nwin, proposal, sfp, grid, stream);

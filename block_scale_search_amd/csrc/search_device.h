@@ -229,20 +229,36 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
     }
 }
 
-// Exhaustive search over all 126 codes, with pruning that provably skips only losers.
-// Each lane first scores the 16 codes around its own base code (octave pairs when the table
-// allows), then extends upward and downward in blocks of 8 codes while the loss bounds above
-// cannot exclude the next code. A bound prunes a direction when it exceeds the best loss by a
-// relative margin of 2^-14, which covers the rounding of the binary32 loss tree and of the
-// bound itself (each at most about 20 roundings of 2^-24 on sums of non-negative terms). The
-// test is used only where that error analysis holds: non-negative finite h, a best loss of at
-// least 2^-100 and amax (1 + max h) <= 2^100 best, so that underflowing products (absolute
-// error 2^-150 each) stay far below the margin; elsewhere the lane scans every code. The result
-// equals the ascending scan of all 126 codes with the first minimum kept.
+// Exhaustive search over all 126 codes, with pruning that provably skips only losers, in three
+// phases per wave.
+//  1. Each lane scores the 16 codes around its own base code (octave pairs when the table
+//     allows) and counts the blocks of 8 codes it still needs above and below them: a block,
+//     and every block beyond it, is skipped when a lower bound on the loss at the block's first
+//     code exceeds the lane's best loss by a relative margin of 2^-14. The margin covers the
+//     rounding of the binary32 loss tree and of the bound itself (each at most about 20
+//     roundings of 2^-24 on sums of non-negative terms). The test is used only where that
+//     error analysis holds: non-negative finite h, a best loss of at least 2^-100 and
+//     amax (1 + max h) <= 2^100 best, so that underflowing products (absolute error 2^-150
+//     each) stay far below the margin; elsewhere the lane needs every block.
+//  2. The wave's pending blocks are dealt over its 64 lanes (a prefix of the per-lane counts
+//     in LDS tells each item's owner), so that the wave runs ceil(total / 64) rounds of 8 codes
+//     instead of as many as its busiest lane needs. A lane scoring another lane's block reloads
+//     that group's weights and h (recently read, so from the caches). Each block's lowest
+//     (loss, code) is merged into its owner's slot with an LDS 64-bit minimum on a key whose
+//     unsigned order is the (loss, code) order (loss_key below), so the merged result does not
+//     depend on the order of the merges.
+//  3. Each lane reads its slot.
+// Every skipped code provably has a larger binary32 loss than the best found, so the result is
+// the lexicographic minimum of (loss, code) over all 126 codes: the ascending scan's first
+// minimum.
+
+// Phase 1 of one lane: the centre block, then the numbers of 8-code blocks needed above
+// (n_up, from code c0 + 16) and below (n_dn, down from code c0 - 1). c0 is returned too.
 template <bool WMSE>
-__device__ __forceinline__ void search_all(const float (&w)[16], const float (&h)[16],
-                                           const float2* __restrict__ tab, bool octave_ok,
-                                           bool live, int b, float& best, int& best_c) {
+__device__ __forceinline__ void exhaustive_centre(const float (&w)[16], const float (&h)[16],
+                                                  const float2* __restrict__ tab, bool octave_ok,
+                                                  bool live, int b, float& best, int& best_c,
+                                                  int& c0, int& n_up, int& n_dn) {
     float amax = 0.0f, hmax = 1.0f;
     bool h_ok = true;
 #pragma unroll
@@ -256,46 +272,60 @@ __device__ __forceinline__ void search_all(const float (&w)[16], const float (&h
     const float scale_ref = amax * (1.0f + hmax);
 
     // centre block: 16 codes from c0 (at least 8 and at most 111 so that pairs stay normal)
-    const int c0 = live ? min(max(b - 8, 8), 111) : 8;
+    c0 = live ? min(max(b - 8, 8), 111) : 8;
     if (octave_ok) {
         scan_block<WMSE, 16>(w, h, tab + c0, c0, 16, best, best_c);
     } else {
         scan8<WMSE>(w, h, tab, c0, best, best_c);
         scan8<WMSE>(w, h, tab, c0 + 8, best, best_c);
     }
-    int up = c0 + 16, dn = c0 - 1;  // next unscored code in each direction
-    bool up_done = !live || up > 126;
-    bool dn_done = !live || dn < 1;
-    while (true) {
-        const bool can_prune = h_ok && best >= 0x1p-100f && scale_ref <= best * 0x1p100f;
-        const float thr = __builtin_fmaf(best, 0x1p-14f, best);
-        if (!up_done && can_prune) {
-            const float B = bound_above<WMSE>(w, h, tab[up].x);
-            up_done = B > thr && B <= 0x1.fffffep127f;
-        }
-        if (up_done && !dn_done && can_prune) {
-            const float B = bound_below<WMSE>(w, h, tab[dn].x);
-            dn_done = B > thr && B <= 0x1.fffffep127f;
-        }
-        const bool go_up = !up_done;
-        const bool go_dn = up_done && !dn_done;
-        if (!__any(go_up || go_dn)) break;
-        const int first = go_up ? up : (go_dn ? dn - 7 : 8);
-        float bl = best;
-        int cl = best_c;
-        scan8<WMSE>(w, h, tab, first, bl, cl);
-        if (go_up || go_dn) {
-            best = bl;
-            best_c = cl;
-        }
-        if (go_up) {
-            up += 8;
-            up_done = up > 126;
-        } else if (go_dn) {
-            dn -= 8;
-            dn_done = dn < 1;
-        }
+    n_up = 0;
+    n_dn = 0;
+    if (!live) return;
+    const int up = c0 + 16, dn = c0 - 1;
+    const int all_up = up <= 126 ? (126 - up) / 8 + 1 : 0;
+    const int all_dn = dn >= 1 ? (dn - 1) / 8 + 1 : 0;
+    const bool can_prune = h_ok && best >= 0x1p-100f && scale_ref <= best * 0x1p100f;
+    if (!can_prune) {
+        n_up = all_up;
+        n_dn = all_dn;
+        return;
     }
+    const float thr = __builtin_fmaf(best, 0x1p-14f, best);
+    while (n_up < all_up) {
+        const float B = bound_above<WMSE>(w, h, tab[up + 8 * n_up].x);
+        if (B > thr && B <= 0x1.fffffep127f) break;
+        ++n_up;
+    }
+    while (n_dn < all_dn) {
+        const float B = bound_below<WMSE>(w, h, tab[dn - 8 * n_dn].x);
+        if (B > thr && B <= 0x1.fffffep127f) break;
+        ++n_dn;
+    }
+}
+
+// (loss, code) as one 64-bit key whose unsigned order is the lexicographic order of the scan:
+// the high word maps the binary32 loss monotonically onto an unsigned value (negative losses,
+// possible with a caller's negative h, below positive ones; -0 and +0 onto the same value, as
+// they compare equal; NaN above everything, as a strict comparison never takes it), then the
+// code, then the loss's sign bit, so that the winner's exact loss (a zero's sign included) can
+// be read back.
+__device__ __forceinline__ uint64_t loss_key(float L, int c) {
+    const uint32_t u = __float_as_uint(L);
+    const uint32_t mag = u & 0x7FFFFFFFu;
+    const uint32_t ord = (L != L) ? 0xFFFFFFFFu
+                         : ((u >> 31) ? 0x80000000u - mag : 0x80000000u + mag);
+    return ((uint64_t)ord << 32) | ((uint64_t)(uint32_t)c << 1) | (uint64_t)(u >> 31);
+}
+
+__device__ __forceinline__ int key_code(uint64_t k) { return (int)((k >> 1) & 0xFFu); }
+
+__device__ __forceinline__ float key_loss(uint64_t k) {
+    const uint32_t ord = (uint32_t)(k >> 32);
+    if (ord == 0xFFFFFFFFu) return __uint_as_float(0x7FC00000u);
+    const uint32_t sign = (uint32_t)(k & 1u) << 31;
+    const uint32_t mag = ord >= 0x80000000u ? ord - 0x80000000u : 0x80000000u - ord;
+    return __uint_as_float(sign | mag);
 }
 
 // Per-workgroup code table in LDS: tab[c] = (eff[c], r[c]) for c = 1..126, tab[0] = (0, 0).
