@@ -132,6 +132,8 @@ def algorithmic_bytes(cfg, label: str) -> int:
         return cfg.batch * cfg.inp * 12
     if label == "h_reduce":
         return T * cfg.inp * 2 + (0 if cfg.chunk_tokens else cfg.batch * cfg.inp * 12)
+    if label == "h_reduce_chunks":
+        return cfg.tokens * cfg.inp * 2 + cfg.inp * 12
     if label == "global_scale":
         return n_w * wb + 4 * cfg.batch
     if label == "h_reduce+global_scale":
@@ -198,17 +200,21 @@ class Kind:
     layer."""
 
     def __init__(self, cfg, n_sets: int, dev, prefix: str, separate_stats: bool,
-                 separate_searches: bool):
+                 separate_searches: bool, h_per_chunk: bool):
         import torch
 
         from block_scale_search_amd import nvfp4, workloads
         self.nv, self.cfg, self.prefix = nvfp4, cfg, prefix
         self.separate_stats, self.separate_searches = separate_stats, separate_searches
+        self.h_per_chunk = h_per_chunk
         self.sets = [Layer(cfg, k, dev) for k in range(n_sets)]
         T = cfg.chunk_tokens or cfg.tokens
         E = cfg.batch
-        self.ws_h = torch.zeros(max(16, nvfp4.nvfp4_diag_hessian_workspace_size(T, cfg.inp, E)),
-                                dtype=torch.uint8, device=dev)
+        ws = nvfp4.nvfp4_diag_hessian_workspace_size(T, cfg.inp, E)
+        if len(self.sets[0].chunks) > 1:
+            ws = max(ws, nvfp4.nvfp4_diag_hessian_chunks_workspace_size(
+                [X.shape[0] for X in self.sets[0].chunks], cfg.inp))
+        self.ws_h = torch.zeros(max(16, ws), dtype=torch.uint8, device=dev)
         self.ws_s = torch.zeros(max(16, nvfp4.nvfp4_global_scale_workspace_size(E, cfg.out,
                                                                                  cfg.inp)),
                                 dtype=torch.uint8, device=dev)
@@ -236,6 +242,10 @@ class Kind:
         n = cfg.inp
         out = []
         deferred = len(s.chunks) > 1 and s.seg is None
+        if deferred and not self.h_per_chunk:
+            # every resident token chunk of the set in one partial launch and one finalize
+            return [("h_reduce_chunks", nv.nvfp4_diag_hessian_chunks(
+                s.chunks, n, n, s.h_acc, s.h, False, self.ws_h, stream=stream, prepare=True))]
         for ci, X in enumerate(s.chunks):
             T = X.shape[0]
             if s.seg is not None:
@@ -486,6 +496,10 @@ def main():
     ap.add_argument("--separate-searches", action="store_true",
                     help="one nvfp4_scale_search call per mode instead of one "
                          "nvfp4_scale_search_rules call for a pair of windowed modes")
+    ap.add_argument("--h-per-chunk", action="store_true",
+                    help="chunked X: one deferred nvfp4_diag_hessian call per token chunk and one "
+                         "finalize, instead of one nvfp4_diag_hessian_chunks call over all of a "
+                         "set's resident chunks")
     ap.add_argument("--schedule", default="pipeline", choices=("pipeline", "sequential"),
                     help="pipeline: the next layer's h and S calls run on a second stream while "
                          "this layer's searches run; sequential: every call on one stream, in "
@@ -529,7 +543,7 @@ def main():
     print(f"# workload {args.workload}: {'; '.join(c.description for c in cfgs)}; {n_sets} "
           f"input set(s)", file=sys.stderr, flush=True)
     kinds = [Kind(c, n_sets, dev, f"{c.name}/" if group else "", args.separate_stats,
-                  args.separate_searches) for c in cfgs]
+                  args.separate_searches, args.h_per_chunk) for c in cfgs]
     torch.cuda.synchronize()
 
     if args.calib_copy:
@@ -678,7 +692,8 @@ def main():
                 "us_per_step": kk["avg_us"], "bytes": kk["alg_bytes"], "GB/s": kk["GB/s"],
                 "frac_hbm": kk["frac_hbm"]}
         else:
-            h_us = kernels[p + "h_reduce"]["avg_us"] * kernels[p + "h_reduce"]["calls_per_step"]
+            lab = p + ("h_reduce_chunks" if p + "h_reduce_chunks" in kernels else "h_reduce")
+            h_us = kernels[lab]["avg_us"] * kernels[lab]["calls_per_step"]
             if p + "h_finalize" in kernels:
                 h_us += kernels[p + "h_finalize"]["avg_us"]
             gbs = x_bytes / h_us / 1e3
@@ -715,6 +730,7 @@ def main():
     for lab in dict.fromkeys(l for l in step_labels if base_label(l).startswith("search")):
         fs = [f for r in range(R) for calls in layer_calls[r] for l, f, _ in calls if l == lab]
         search_alone[lab] = back_to_back(fs, max(4, 3 * len(fs)))
+        kernels[lab]["alone_us"] = round(search_alone[lab], 3)
 
     # roofline: the fixed-work search (same mode over every matrix of the step) with the
     # largest share of the step

@@ -148,6 +148,42 @@ nvfp4_status nvfp4_diag_hessian_batched(const void* X, int x_dtype, const int64_
                              accumulate, workspace, workspace_bytes, stream);
 }
 
+size_t nvfp4_diag_hessian_chunks_workspace_size(const int64_t* tokens, int64_t n_chunks,
+                                                int64_t in) {
+    if (tokens == nullptr || n_chunks < 1 || n_chunks > nvfp4::kMaxHessianChunks || in < 0)
+        return 0;
+    for (int64_t c = 0; c < n_chunks; ++c)
+        if (tokens[c] < 0) return 0;
+    return nvfp4::hessian_chunks_workspace_bytes(tokens, n_chunks, in);
+}
+
+nvfp4_status nvfp4_diag_hessian_chunks(const void* const* X_chunks, int x_dtype,
+                                       const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                       int64_t ldx, double* h_acc, float* h, int accumulate,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+    if (elem_size(x_dtype) == 0) return NVFP4_ERR_DTYPE;
+    if (X_chunks == nullptr || tokens == nullptr) return NVFP4_ERR_NULL;
+    if (n_chunks < 1 || n_chunks > nvfp4::kMaxHessianChunks || in < 0) return NVFP4_ERR_SHAPE;
+    if (in % 8 != 0 || ldx < in || ldx % 8 != 0) return NVFP4_ERR_SHAPE;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        if (tokens[c] < 0 || !span_ok(tokens[c], ldx)) return NVFP4_ERR_SHAPE;
+        if (tokens[c] > 0 && in > 0 && X_chunks[c] == nullptr) return NVFP4_ERR_NULL;
+        if (X_chunks[c] && !aligned16(X_chunks[c])) return NVFP4_ERR_ALIGN;
+    }
+    if (in == 0) return NVFP4_OK;
+    if (h_acc == nullptr) return NVFP4_ERR_NULL;
+    if (!aligned8(h_acc) || (h && (reinterpret_cast<uintptr_t>(h) & 3u))) return NVFP4_ERR_ALIGN;
+    const bool bf16 = x_dtype == NVFP4_DTYPE_BF16;
+    if (nvfp4::hessian_chunks_launch_blocks(tokens, n_chunks, in, bf16) >= ((int64_t)1 << 31))
+        return NVFP4_ERR_SHAPE;
+    const size_t need = nvfp4::hessian_chunks_workspace_bytes(tokens, n_chunks, in);
+    if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return NVFP4_ERR_WORKSPACE;
+    if (workspace && !aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_diag_hessian_chunks(X_chunks, bf16, tokens, n_chunks, in, ldx,
+                                                        h_acc, h, accumulate != 0, workspace,
+                                                        static_cast<hipStream_t>(stream)));
+}
+
 size_t nvfp4_global_scale_workspace_size(int64_t batch, int64_t out, int64_t in) {
     if (batch < 0 || out < 0 || in < 0) return 0;
     return nvfp4::global_scale_workspace_bytes(batch, out, in);

@@ -62,6 +62,15 @@ struct GroupMap {
     int64_t single_groups;       // one segment: its group count
 };
 
+// Token chunks of one set at separate addresses (one partial launch over all of them).
+struct ChunkTable {
+    const uint8_t* x[kMaxHessianChunks];
+    int64_t tokens[kMaxHessianChunks];
+    int32_t blk_prefix[kMaxHessianChunks + 1];   // first workgroup of each chunk
+    int32_t slot_prefix[kMaxHessianChunks + 1];  // first workspace slot of each chunk
+    int32_t n;
+};
+
 __host__ __device__ __forceinline__ int64_t groups_for(int64_t rows, int64_t rows_per_group) {
     return rows > 0 ? (rows + rows_per_group - 1) / rows_per_group : 0;
 }
@@ -254,6 +263,24 @@ __global__ __launch_bounds__(kFinThreads) void k_hess_finalize(const double* __r
     hess_finalize_body(partial, in, map, h_acc, h, accumulate, blockIdx.x, blockIdx.y, red);
 }
 
+// Several token chunks of one set at separate addresses, in one partial launch: workgroups
+// [blk_prefix[c], blk_prefix[c + 1]) run the single-segment partial pass over chunk c into the
+// slots [slot_prefix[c], slot_prefix[c + 1]); one finalize then sums every slot.
+template <bool BF16, int V>
+__global__ __launch_bounds__(64 * V) void k_hess_partial_chunks(ChunkTable ct, int64_t in,
+                                                                int64_t ldx_bytes,
+                                                                int64_t n_strips,
+                                                                double* __restrict__ partial) {
+    __shared__ double red[V][XCols<BF16>::kStrip];
+    const int32_t blk = (int32_t)blockIdx.x;
+    int c = 0;                                   // chunk of this workgroup (uniform)
+    while (c + 1 < ct.n && ct.blk_prefix[c + 1] <= blk) ++c;
+    const int32_t slot0 = ct.slot_prefix[c];
+    GroupMap map{nullptr, nullptr, 1, ct.tokens[c], 0, ct.slot_prefix[c + 1] - slot0};
+    hess_partial_body<BF16, V>(ct.x[c], in, ldx_bytes, map, n_strips, partial + (int64_t)slot0 * in,
+                               0, blk - ct.blk_prefix[c], red);
+}
+
 // Layer statistics, pass 1: the first n_hess workgroups are the h partial pass over X, the rest
 // the amax partial pass over W (both streaming, one launch).
 template <bool XBF16, int V, bool WBF16>
@@ -378,6 +405,86 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
     }
     if (pass == HessianPass::kPartial) return hipGetLastError();
     const dim3 fgrid((uint32_t)((in + kFinCols - 1) / kFinCols), (uint32_t)E);
+    hipLaunchKernelGGL(k_hess_finalize, fgrid, dim3(kFinThreads), 0, stream, partial, in, map,
+                       h_acc, h, accumulate ? 1 : 0);
+    return hipGetLastError();
+}
+
+// Chunks: rows per group chosen over the whole set (about kTargetGroups workgroups in all, as
+// for the segments of a batch), each chunk with ceil(tokens / rows_per_group) groups.
+static bool plan_chunks(const int64_t* tokens, int64_t n_chunks, int64_t in, bool bf16,
+                        ChunkTable* ct, int64_t* slots, int64_t* blocks) {
+    int64_t total = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) total += tokens[c];
+    const int64_t rpg = rows_per_group(total, in, bf16);
+    const int64_t strips = strips_for(in, bf16);
+    int64_t s = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+        if (ct) {
+            ct->slot_prefix[c] = (int32_t)s;
+            ct->blk_prefix[c] = (int32_t)(s * strips);
+            ct->tokens[c] = tokens[c];
+        }
+        s += groups_for(tokens[c], rpg);
+        if (s * strips >= ((int64_t)1 << 31)) return false;
+    }
+    if (ct) {
+        ct->slot_prefix[n_chunks] = (int32_t)s;
+        ct->blk_prefix[n_chunks] = (int32_t)(s * strips);
+        ct->n = (int32_t)n_chunks;
+    }
+    *slots = s;
+    *blocks = s * strips;
+    return true;
+}
+
+size_t hessian_chunks_workspace_bytes(const int64_t* tokens, int64_t n_chunks, int64_t in) {
+    // sized for the element type with more row groups, so one size serves both
+    int64_t s32 = 0, s16 = 0, b = 0;
+    if (!plan_chunks(tokens, n_chunks, in, false, nullptr, &s32, &b) ||
+        !plan_chunks(tokens, n_chunks, in, true, nullptr, &s16, &b))
+        return 0;
+    return (size_t)(s32 > s16 ? s32 : s16) * (size_t)in * sizeof(double);
+}
+
+int64_t hessian_chunks_launch_blocks(const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                     bool bf16) {
+    int64_t s = 0, b = 0;
+    if (!plan_chunks(tokens, n_chunks, in, bf16, nullptr, &s, &b)) return (int64_t)1 << 31;
+    return b;
+}
+
+hipError_t launch_diag_hessian_chunks(const void* const* X_chunks, bool bf16,
+                                      const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                      int64_t ldx, double* h_acc, float* h, bool accumulate,
+                                      void* workspace, hipStream_t stream) {
+    ChunkTable ct{};
+    int64_t slots = 0, blocks = 0;
+    if (!plan_chunks(tokens, n_chunks, in, bf16, &ct, &slots, &blocks)) return hipErrorInvalidValue;
+    for (int64_t c = 0; c < n_chunks; ++c) ct.x[c] = static_cast<const uint8_t*>(X_chunks[c]);
+    double* partial = static_cast<double*>(workspace);
+    const int64_t n_strips = strips_for(in, bf16);
+    const int64_t ldx_bytes = ldx * (bf16 ? 2 : 4);
+    int64_t total = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) total += tokens[c];
+    const bool wide = total * in * (bf16 ? 2 : 4) >= kWideBytes;
+    if (blocks > 0) {
+        const dim3 grid((uint32_t)blocks);
+        if (bf16 && wide)
+            hipLaunchKernelGGL((k_hess_partial_chunks<true, 4>), grid, dim3(256), 0, stream, ct,
+                               in, ldx_bytes, n_strips, partial);
+        else if (bf16)
+            hipLaunchKernelGGL((k_hess_partial_chunks<true, 8>), grid, dim3(512), 0, stream, ct,
+                               in, ldx_bytes, n_strips, partial);
+        else if (wide)
+            hipLaunchKernelGGL((k_hess_partial_chunks<false, 4>), grid, dim3(256), 0, stream, ct,
+                               in, ldx_bytes, n_strips, partial);
+        else
+            hipLaunchKernelGGL((k_hess_partial_chunks<false, 8>), grid, dim3(512), 0, stream, ct,
+                               in, ldx_bytes, n_strips, partial);
+    }
+    const GroupMap map{nullptr, nullptr, 1, total, 0, slots};
+    const dim3 fgrid((uint32_t)((in + kFinCols - 1) / kFinCols), 1u);
     hipLaunchKernelGGL(k_hess_finalize, fgrid, dim3(kFinThreads), 0, stream, partial, in, map,
                        h_acc, h, accumulate ? 1 : 0);
     return hipGetLastError();

@@ -30,6 +30,17 @@ hipError_t launch_diag_hessian(const void* X, bool bf16, int64_t tokens, int64_t
                                float* h, bool accumulate, void* workspace, hipStream_t stream,
                                HessianPass pass = HessianPass::kBoth);
 
+// Token chunks of one set at separate addresses: one partial launch over all of them, then
+// one finalize. Workspace bytes (0 if the plan does not fit) and partial workgroup count.
+constexpr int kMaxHessianChunks = 64;
+size_t hessian_chunks_workspace_bytes(const int64_t* tokens, int64_t n_chunks, int64_t in);
+int64_t hessian_chunks_launch_blocks(const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                     bool bf16);
+hipError_t launch_diag_hessian_chunks(const void* const* X_chunks, bool bf16,
+                                      const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                      int64_t ldx, double* h_acc, float* h, bool accumulate,
+                                      void* workspace, hipStream_t stream);
+
 size_t global_scale_workspace_bytes(int64_t batch, int64_t out, int64_t in);
 hipError_t launch_global_scale(const void* W, bool bf16, int64_t batch, int64_t out, int64_t in,
                                int64_t ldw, int64_t stride_w, int rule, float* S, void* workspace,

@@ -45,6 +45,8 @@ _SIGS = {
     "nvfp4_diag_hessian": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_diag_hessian_finalize": ([_I, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_diag_hessian_batched": ([_P, _I, _P, _I64, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
+    "nvfp4_diag_hessian_chunks_workspace_size": ([_P, _I64, _I64], _SZ),
+    "nvfp4_diag_hessian_chunks": ([_P, _I, _P, _I64, _I64, _I64, _P, _P, _I, _P, _SZ, _P], _I),
     "nvfp4_global_scale_workspace_size": ([_I64, _I64, _I64], _SZ),
     "nvfp4_global_scale": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I, _P, _P, _SZ, _P], _I),
     "nvfp4_layer_statistics_workspace_size": ([_I64, _I64, _I64], _SZ),
@@ -138,6 +140,35 @@ def nvfp4_status_string(status: int) -> str:
 
 def nvfp4_diag_hessian_workspace_size(tokens: int, inp: int, segments: int = 1) -> int:
     return int(_lib.nvfp4_diag_hessian_workspace_size(tokens, inp, segments))
+
+
+def _i64_array(values):
+    return (ctypes.c_int64 * len(values))(*[int(v) for v in values])
+
+
+def nvfp4_diag_hessian_chunks_workspace_size(tokens, inp: int) -> int:
+    t = _i64_array(tokens)
+    return int(_lib.nvfp4_diag_hessian_chunks_workspace_size(t, len(tokens), inp))
+
+
+def nvfp4_diag_hessian_chunks(X_chunks, inp, ldx, h_acc, h, accumulate, workspace, stream=None,
+                              prepare=False):
+    """h over several token chunks (tensors [tokens_c, in] at separate addresses) in one partial
+    launch and one finalize."""
+    if not X_chunks:
+        raise ValueError("at least one chunk")
+    dt = {_wdtype(X) for X in X_chunks}
+    if len(dt) != 1:
+        raise TypeError("every chunk must have the same element type")
+    _need(h_acc, inp, "h_acc")
+    if h is not None:
+        _need(h, inp, "h")
+    ptrs = (ctypes.c_void_p * len(X_chunks))(*[_dev(X, "X").value for X in X_chunks])
+    toks = _i64_array([X.shape[0] for X in X_chunks])
+    args = (ptrs, dt.pop(), toks, len(X_chunks), inp, ldx, _dev(h_acc, "h_acc", (torch.float64,)),
+            _dev(h, "h", (torch.float32,)), int(accumulate), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream))
+    return _run("nvfp4_diag_hessian_chunks", args, prepare)
 
 
 def nvfp4_global_scale_workspace_size(batch: int, out: int, inp: int) -> int:

@@ -108,6 +108,29 @@ nvfp4_status nvfp4_diag_hessian_finalize(int x_dtype, int64_t tokens, int64_t in
                                          float* h, int accumulate, void* workspace,
                                          size_t workspace_bytes, void* stream);
 
+/* Token chunks of one calibration set that are resident together but not contiguous (e.g. the
+ * activations of several forward passes), reduced in one partial launch and one finalize
+ * instead of one launch per chunk ([HS] §4: the one-time activation pass over the calibration
+ * set; App. B: h = diag(X^T X)):
+ *   h_acc[j] = (accumulate ? h_acc[j] : 0) + sum_c sum_{t < tokens[c]} X_c[t, j]^2   (binary64)
+ *   h[j]     = (float) h_acc[j]
+ * X_chunks  host array of n_chunks device pointers (read during the call only); chunk c is
+ *           [tokens[c], in] with row stride ldx, bf16 or f32 (x_dtype), 16-byte aligned.
+ * tokens    host array of n_chunks token counts (>= 0). 1 <= n_chunks <= 64.
+ * h_acc, h, accumulate  as for nvfp4_diag_hessian (h_acc required).
+ * workspace at least nvfp4_diag_hessian_chunks_workspace_size(tokens, n_chunks, in) bytes,
+ *           16-byte aligned; overwritten, no initialisation needed. The size function returns
+ *           0 for invalid arguments.
+ * Deterministic. The binary64 partial sums are grouped differently from a sequence of
+ * per-chunk calls, so the two agree to binary64 rounding, not always bit for bit. */
+size_t nvfp4_diag_hessian_chunks_workspace_size(const int64_t* tokens, int64_t n_chunks,
+                                                int64_t in);
+
+nvfp4_status nvfp4_diag_hessian_chunks(const void* const* X_chunks, int x_dtype,
+                                       const int64_t* tokens, int64_t n_chunks, int64_t in,
+                                       int64_t ldx, double* h_acc, float* h, int accumulate,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Batched form for a mixture-of-experts layer: X holds the routed tokens of `segments` experts
  * back to back; expert e owns rows [seg_offsets[e], seg_offsets[e+1]). Writes h_acc/h as
  * [segments, in] (row e = expert e), with the same accumulate rule per row.

@@ -327,3 +327,33 @@ def test_deferred_hessian_slots_never_shrink_with_tokens(lib):
             assert sizes[t] >= sizes[t - 1], (inp, t)
         # the shapes the advisor found out of order: 1025 vs 1024 and 7936 vs 7680 tokens
         assert sizes[1025] >= sizes[1024] and sizes[7936] >= sizes[7680]
+
+
+def test_diag_hessian_chunks_rejects_bad_arguments(lib):
+    """The one-launch form over token chunks validates every chunk on the host."""
+    from block_scale_search_amd import nvfp4 as n
+    T = (ctypes.c_int64 * 3)(100, 0, 50)
+    need = lib.nvfp4_diag_hessian_chunks_workspace_size(T, 3, 64)
+    assert need > 0
+    assert lib.nvfp4_diag_hessian_chunks_workspace_size(T, 0, 64) == 0
+    assert lib.nvfp4_diag_hessian_chunks_workspace_size(T, 65, 64) == 0
+
+    def call(ptrs=(FAKE, None, FAKE), toks=(100, 0, 50), **kw):
+        a = dict(xd=1, inp=64, ldx=64, acc=FAKE, h=FAKE, ws=FAKE, wsb=need)
+        a.update(kw)
+        P = (ctypes.c_void_p * len(ptrs))(*[None if p is None else p.value for p in ptrs])
+        t = (ctypes.c_int64 * len(toks))(*toks)
+        return lib.nvfp4_diag_hessian_chunks(P, a["xd"], t, len(toks), a["inp"], a["ldx"],
+                                             a["acc"], a["h"], 0, a["ws"], a["wsb"], None)
+    assert call(xd=5) == n.ERR_DTYPE
+    assert call(ptrs=(), toks=()) == n.ERR_SHAPE
+    assert call(inp=60, ldx=64) == n.ERR_SHAPE
+    assert call(ldx=32) == n.ERR_SHAPE
+    assert call(toks=(100, -1, 50)) == n.ERR_SHAPE
+    assert call(ptrs=(FAKE, None, None)) == n.ERR_NULL       # a chunk with tokens needs data
+    assert call(ptrs=(FAKE, None, ODD)) == n.ERR_ALIGN
+    assert call(acc=None) == n.ERR_NULL
+    assert call(wsb=need - 1) == n.ERR_WORKSPACE
+    assert call(inp=0) == n.OK
+    assert lib.nvfp4_diag_hessian_chunks(None, 1, T, 3, 64, 64, FAKE, FAKE, 0, FAKE, need,
+                                         None) == n.ERR_NULL

@@ -415,3 +415,34 @@ def test_hessian_deferred_ragged_chunks(nv, inp, sizes, ws_tokens):
     acc_o, h_o = oracle.diag_hessian(host_w(torch.cat(chunks)))
     np.testing.assert_allclose(h_acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
     np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("inp,sizes,ldx", [
+    (4096, [8192] * 8, 4096),                   # the 70B-shaped calibration set's chunk shape
+    (1040, [3000, 0, 17, 1234, 1], 1040),       # ragged sizes, an empty chunk
+    (640, [2500, 700], 704),                     # padded rows
+    (24, [1], 24),                               # one chunk of one token
+])
+def test_hessian_chunks_one_launch(nv, dtype, inp, sizes, ldx):
+    """Chunks at separate addresses in one partial launch and one finalize: h over all their
+    tokens against the oracle (binary64 sums within 1e-12, h within 1e-5), and accumulate
+    continues from h_acc."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(sum(sizes) + inp + ldx)
+    sig = torch.exp(torch.randn(inp, generator=g, device=DEV) * 1.5)
+    full = [(torch.randn((t, ldx), generator=g, device=DEV) *
+             torch.nn.functional.pad(sig, (0, ldx - inp), value=1.0)).to(dtype) for t in sizes]
+    chunks = [f[:, :inp] for f in full]
+    ws = torch.empty(max(16, nv.nvfp4_diag_hessian_chunks_workspace_size(sizes, inp)),
+                     dtype=torch.uint8, device=DEV)
+    h_acc = torch.empty(inp, dtype=torch.float64, device=DEV)
+    h = torch.empty(inp, dtype=torch.float32, device=DEV)
+    nv.nvfp4_diag_hessian_chunks(chunks, inp, ldx, h_acc, h, False, ws)
+    torch.cuda.synchronize()
+    acc_o, h_o = oracle.diag_hessian(host_w(torch.cat(chunks)))
+    np.testing.assert_allclose(h_acc.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
+    np.testing.assert_allclose(h.cpu().numpy(), h_o, rtol=H_RTOL, atol=0)
+    nv.nvfp4_diag_hessian_chunks(chunks, inp, ldx, h_acc, None, True, ws)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(h_acc.cpu().numpy(), 2 * acc_o, rtol=1e-12, atol=0)
