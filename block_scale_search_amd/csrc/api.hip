@@ -3,6 +3,8 @@
 // leave work behind.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "../../include/nvfp4.h"
 #include "internal.h"
 
@@ -361,11 +363,17 @@ size_t nvfp4_quantize_activations_workspace_size(int64_t tokens, int64_t in) {
     return 256 + (size_t)nvfp4::amax_partial_count(1, tokens, in) * sizeof(uint32_t);
 }
 
-nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
-                                        int64_t ldx, int objective, const float* h, int32_t lo,
-                                        int32_t hi, int rule, float* S_out, uint8_t* scales,
-                                        uint8_t* packed, void* workspace, size_t workspace_bytes,
-                                        void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation and launches shared by nvfp4_quantize_activations and its allocation-free variant;
+// `workspace` holds [S slot, 256 B][amax partials] of the size
+// nvfp4_quantize_activations_workspace_size returns (already checked by the caller).
+nvfp4_status check_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                               int64_t ldx, int objective, const float* h, int32_t lo, int32_t hi,
+                               int rule, const float* S_out, const uint8_t* scales,
+                               const uint8_t* packed) {
     if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
     if (rule != NVFP4_GS_AMAX_448 && rule != NVFP4_GS_AMAX_256) return NVFP4_ERR_ARG;
     if (lo > 0 || hi < 0 || lo < -125 || hi > 125) return NVFP4_ERR_WINDOW;
@@ -377,9 +385,14 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
     if (!aligned8(packed) || (S_out && (reinterpret_cast<uintptr_t>(S_out) & 3u)) ||
         (wmse && !aligned16(h)))
         return NVFP4_ERR_ALIGN;
-    const size_t need = nvfp4_quantize_activations_workspace_size(tokens, in);
-    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+nvfp4_status launch_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                int64_t ldx, int objective, const float* h, int32_t lo,
+                                int32_t hi, int rule, float* S_out, uint8_t* scales,
+                                uint8_t* packed, void* workspace, void* stream) {
+    const bool wmse = objective == NVFP4_WMSE;
     const bool bf16 = x_dtype == NVFP4_DTYPE_BF16;
     hipStream_t s = static_cast<hipStream_t>(stream);
     float* S_slot = static_cast<float*>(workspace);
@@ -404,6 +417,68 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
                                                  wmse ? h : nullptr, 0, wmse, lo, hi, false, src,
                                                  scales, packed, nullptr, nullptr, nullptr,
                                                  nullptr, s));
+}
+
+// Scratch of nvfp4_quantize_activations_noalloc, one copy per GPU for the life of the process:
+// the S slot (256 B) and the amax partials (at most 512 x 4 B), the same layout as the caller's
+// workspace of nvfp4_quantize_activations.
+constexpr size_t kNoAllocScratchBytes = 4096;
+__device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+// In host code `scratch` names a host-side stand-in for the symbol, not a device address: the
+// address of each GPU's copy is looked up once per device, with that device current, and kept.
+constexpr int kMaxScratchDevices = 64;
+std::once_flag g_scratch_once[kMaxScratchDevices];
+void* g_scratch_ptr[kMaxScratchDevices];
+hipError_t g_scratch_status[kMaxScratchDevices];
+
+hipError_t current_device_scratch(void** ptr) {
+    int dev = -1;
+    const hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* p = nullptr;
+        g_scratch_status[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = p;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_ptr[dev] != nullptr ? g_scratch_status[dev] : hipErrorInvalidSymbol;
+}
+
+}  // namespace
+
+extern "C" {
+
+nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t tokens, int64_t in,
+                                        int64_t ldx, int objective, const float* h, int32_t lo,
+                                        int32_t hi, int rule, float* S_out, uint8_t* scales,
+                                        uint8_t* packed, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+    const nvfp4_status st = check_activations(X, x_dtype, tokens, in, ldx, objective, h, lo, hi,
+                                              rule, S_out, scales, packed);
+    if (st != NVFP4_OK || tokens == 0 || in == 0) return st;
+    const size_t need = nvfp4_quantize_activations_workspace_size(tokens, in);
+    if (workspace == nullptr || workspace_bytes < need) return NVFP4_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return NVFP4_ERR_ALIGN;
+    return launch_activations(X, x_dtype, tokens, in, ldx, objective, h, lo, hi, rule, S_out,
+                              scales, packed, workspace, stream);
+}
+
+nvfp4_status nvfp4_quantize_activations_noalloc(const void* X, int x_dtype, int64_t tokens,
+                                                int64_t in, int64_t ldx, int objective,
+                                                const float* h, int32_t lo, int32_t hi, int rule,
+                                                float* S_out, uint8_t* scales, uint8_t* packed,
+                                                void* stream) {
+    const nvfp4_status st = check_activations(X, x_dtype, tokens, in, ldx, objective, h, lo, hi,
+                                              rule, S_out, scales, packed);
+    if (st != NVFP4_OK || tokens == 0 || in == 0) return st;
+    if (nvfp4_quantize_activations_workspace_size(tokens, in) > kNoAllocScratchBytes)
+        return NVFP4_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (current_device_scratch(&ws) != hipSuccess) return NVFP4_ERR_HIP;
+    return launch_activations(X, x_dtype, tokens, in, ldx, objective, h, lo, hi, rule, S_out,
+                              scales, packed, ws, stream);
 }
 
 size_t nvfp4_gptq_workspace_size(int64_t out, int64_t in) {

@@ -62,6 +62,8 @@ _SIGS = {
     "nvfp4_quantize_activations_workspace_size": ([_I64, _I64], _SZ),
     "nvfp4_quantize_activations": ([_P, _I, _I64, _I64, _I64, _I, _P, _I32, _I32, _I, _P, _P, _P,
                                     _P, _SZ, _P], _I),
+    "nvfp4_quantize_activations_noalloc": ([_P, _I, _I64, _I64, _I64, _I, _P, _I32, _I32, _I,
+                                            _P, _P, _P, _P], _I),
     "nvfp4_gptq_workspace_size": ([_I64, _I64], _SZ),
     "nvfp4_gptq": ([_P, _I, _I64, _I64, _I64, _P, _P, _I, _I32, _I32, _P, _P, _P, _P, _P, _SZ,
                     _P], _I),
@@ -331,6 +333,20 @@ def nvfp4_quantize_activations(X, tokens, inp, ldx, objective, h, lo, hi, rule, 
         _dev(h, "h", (torch.float32,)), lo, hi, rule, _dev(S_out, "S_out", (torch.float32,)),
         _dev(scales, "scales", (torch.uint8,)), _dev(packed, "packed", (torch.uint8,)),
         _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)), prepare)
+
+
+def nvfp4_quantize_activations_noalloc(X, tokens, inp, ldx, objective, h, lo, hi, rule, S_out,
+                                       scales, packed, stream=None, prepare=False):
+    """nvfp4_quantize_activations without a workspace: the library's own per-GPU scratch (no
+    allocation; calls that overlap on one GPU race)."""
+    G = tokens * (inp // 16)
+    _need(scales, G, "scales")
+    _need(packed, G * 8, "packed")
+    return _run("nvfp4_quantize_activations_noalloc", (
+        _dev(X, "X", (torch.float32, torch.bfloat16)), _wdtype(X), tokens, inp, ldx, objective,
+        _dev(h, "h", (torch.float32,)), lo, hi, rule, _dev(S_out, "S_out", (torch.float32,)),
+        _dev(scales, "scales", (torch.uint8,)), _dev(packed, "packed", (torch.uint8,)),
         _stream(stream)), prepare)
 
 

@@ -367,6 +367,28 @@ nvfp4_status nvfp4_quantize_activations(const void* X, int x_dtype, int64_t toke
                                         void* stream);
 
 /* ---------------------------------------------------------------------------------------------
+ * nvfp4_quantize_activations without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc. Arguments, outputs and errors are those of
+ * nvfp4_quantize_activations (outputs bit-identical), minus the workspace.
+ *
+ * Scratch: a 4096-byte device array in the library, one copy per GPU, held until the process
+ * ends; the call uses the copy of the device current at the call (the device `stream` belongs
+ * to must be current). The activation call needs at most 2304 bytes of it (the S slot and at
+ * most 512 amax partials), whatever the tensor's size; a need above 4096 bytes would return
+ * NVFP4_ERR_WORKSPACE. Every call overwrites the scratch bytes it reads, so nothing needs
+ * clearing, but all calls on one GPU share the one array: calls that overlap in time on one GPU
+ * (on different streams, or from different threads) race and must be serialised by the caller.
+ * The first call on a device looks the array's device address up once (no allocation); it
+ * returns NVFP4_ERR_HIP if that fails.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_quantize_activations_noalloc(const void* X, int x_dtype, int64_t tokens,
+                                                int64_t in, int64_t ldx, int objective,
+                                                const float* h, int32_t lo, int32_t hi, int rule,
+                                                float* S_out, uint8_t* scales, uint8_t* packed,
+                                                void* stream);
+
+/* ---------------------------------------------------------------------------------------------
  * Evaluation: layer-output error of a quantised layer ([HS] §3: the layer-output reconstruction
  * criterion; the activation-loss comparison of Min-Max, MSE-guided and Hessian-guided scales).
  *

@@ -213,6 +213,35 @@ def test_quantize_activations_rejects_bad_arguments(lib):
     assert call(T=0, X=None) == n.OK
 
 
+def test_quantize_activations_noalloc_rejects_bad_arguments(lib):
+    """The allocation-free variant validates exactly as the workspace call does, before it
+    touches the device; its scratch (S slot and at most 512 amax partials) fits the library's
+    4096-byte array at every size, the largest included."""
+    from block_scale_search_amd import nvfp4 as n
+
+    def call(**kw):
+        a = dict(X=FAKE, xd=1, T=32, inp=64, ldx=64, obj=0, h=None, lo=-3, hi=7, rule=1, S=FAKE,
+                 sc=FAKE, pk=FAKE)
+        a.update(kw)
+        return lib.nvfp4_quantize_activations_noalloc(a["X"], a["xd"], a["T"], a["inp"],
+                                                      a["ldx"], a["obj"], a["h"], a["lo"],
+                                                      a["hi"], a["rule"], a["S"], a["sc"],
+                                                      a["pk"], None)
+    assert call(obj=3) == n.ERR_ARG
+    assert call(rule=2) == n.ERR_ARG
+    assert call(lo=1) == n.ERR_WINDOW
+    assert call(hi=126) == n.ERR_WINDOW
+    assert call(xd=7) == n.ERR_DTYPE
+    assert call(inp=40, ldx=40) == n.ERR_SHAPE
+    assert call(T=1 << 28, inp=1 << 12, ldx=1 << 12) == n.ERR_SHAPE   # groups >= 2^31
+    assert call(obj=1) == n.ERR_NULL
+    assert call(pk=None) == n.ERR_NULL
+    assert call(X=ODD) == n.ERR_ALIGN
+    assert call(T=0, X=None) == n.OK
+    for T, inp in ((1, 16), (16, 2048), (8192, 8192), ((1 << 27) - 1, 256)):
+        assert lib.nvfp4_quantize_activations_workspace_size(T, inp) <= 4096
+
+
 def test_hessian_finalize_rejects_bad_arguments(lib):
     from block_scale_search_amd import nvfp4 as n
     f = lib.nvfp4_diag_hessian_finalize
