@@ -266,10 +266,11 @@ class Kind:
                 stream=stream, prepare=True)))
         return out
 
-    def calls(self, s, stage=None):
+    def calls(self, s, stage=None, search=None):
         """One layer as (label, call, role) triples in issue order; each call is a prepared C-ABI
         invocation (arguments marshalled once). Role "stage": produces h and S (on the stage
-        stream under the pipeline); role "main": the searches."""
+        stream under the pipeline); role "main": the searches (on `search`, default the current
+        stream)."""
         nv, cfg = self.nv, self.cfg
         b, o, n = cfg.batch, cfg.out, cfg.inp
         ldw, sw = n, o * n
@@ -295,7 +296,7 @@ class Kind:
                      for m, i in zip(pair, idx)]
             out.append((pair_label(pair), nv.nvfp4_scale_search_rules(
                 s.W, b, o, n, ldw, sw, 16, s.h if wm_any else None, n if wm_any else 0, s.S,
-                rules, prepare=True), "main"))
+                rules, stream=search, prepare=True), "main"))
         for mi, m in enumerate(cfg.modes):
             wm = m.objective == "wmse"
             if pair is not None and m in pair:
@@ -304,12 +305,12 @@ class Kind:
                 out.append((f"search:{m.label}", nv.nvfp4_scale_search_proposal(
                     s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
                     nv.WMSE if wm else nv.MSE, m.lo, m.hi, s.center, s.incoming, s.S,
-                    s.scales[mi], s.packed[mi], prepare=True), "main"))
+                    s.scales[mi], s.packed[mi], stream=search, prepare=True), "main"))
                 continue
             out.append((f"search:{m.label}", nv.nvfp4_scale_search(
                 s.W, b, o, n, ldw, sw, 16, s.h if wm else None, n if wm else 0,
                 nv.WMSE if wm else nv.MSE, m.lo, m.hi, m.exhaustive, s.S, s.scales[mi],
-                s.packed[mi], prepare=True), "main"))
+                s.packed[mi], stream=search, prepare=True), "main"))
         return [(self.prefix + lab, f, role) for lab, f, role in out]
 
 
@@ -504,6 +505,10 @@ def main():
                     help="pipeline: the next layer's h and S calls run on a second stream while "
                          "this layer's searches run; sequential: every call on one stream, in "
                          "order")
+    ap.add_argument("--search-streams", type=int, default=1, choices=(1, 2),
+                    help="layer pipeline: consecutive layers' searches on 1 stream, or on 2 "
+                         "alternating streams so that one layer's search starts while the "
+                         "previous one's last workgroups finish")
     ap.add_argument("--events-every", type=int, default=8,
                     help="record per-call HIP events on every Nth timed step (1 = all)")
     ap.add_argument("--calib-copy", action="store_true",
@@ -559,8 +564,15 @@ def main():
     stage = torch.cuda.Stream() if pipelined else None
     R = len(kinds)
     # layer j of the rotation: matrix kind j % R, input set (j // R) % n_sets; step i = layers
-    # i R .. i R + R - 1
-    layer_calls = [[kd.calls(s, stage) for s in kd.sets] for kd in kinds]
+    # i R .. i R + R - 1. With two search streams, layer j's searches run on stream
+    # (j mod R n_sets) mod 2, which alternates between consecutive layers when R n_sets is even.
+    search_sts = [main_st] + ([torch.cuda.Stream()] if pipelined and args.search_streams == 2
+                              else [])
+
+    def search_stream(r, k):
+        return search_sts[(r + R * k) % len(search_sts)]
+    layer_calls = [[kd.calls(s, stage, search_stream(r, k)) for k, s in enumerate(kd.sets)]
+                   for r, kd in enumerate(kinds)]
     step_labels = [lab for r in range(R) for lab, _, _ in layer_calls[r][0]]
 
     def calls_of(j):
@@ -608,17 +620,22 @@ def main():
             ev_stage[r][k].record(stage)
 
         stage.wait_stream(main_st)
+        for st in search_sts[1:]:
+            st.wait_stream(main_st)
         issue_stage(j0)
         for j in range(j0, j1):
             r, k = j % R, (j // R) % n_sets
             if j + 1 < j1:
                 issue_stage(j + 1)
-            main_st.wait_event(ev_stage[r][k])
+            st = search_stream(r, k)
+            st.wait_event(ev_stage[r][k])
             for lab, f, role in calls_of(j):
                 if role != "stage":
-                    timed_call(lab, f, main_st, row_of(j))
-            ev_done[r][k].record(main_st)
+                    timed_call(lab, f, st, row_of(j))
+            ev_done[r][k].record(st)
         main_st.wait_stream(stage)
+        for st in search_sts[1:]:
+            main_st.wait_stream(st)
 
     run_layers(0, args.warmup)
     torch.cuda.synchronize()
@@ -727,8 +744,9 @@ def main():
             "GB/s": round(pack_bytes / pack_us / 1e3, 1),
             "frac_hbm": round(pack_bytes / pack_us / 1e3 / HBM_PEAK_GBS, 4)}
     search_alone = {}
+    alone_calls = [[kd.calls(s) for s in kd.sets] for kd in kinds]   # all on the main stream
     for lab in dict.fromkeys(l for l in step_labels if base_label(l).startswith("search")):
-        fs = [f for r in range(R) for calls in layer_calls[r] for l, f, _ in calls if l == lab]
+        fs = [f for r in range(R) for calls in alone_calls[r] for l, f, _ in calls if l == lab]
         search_alone[lab] = back_to_back(fs, max(4, 3 * len(fs)))
         kernels[lab]["alone_us"] = round(search_alone[lab], 3)
 
@@ -837,6 +855,7 @@ def main():
                    "layer_weights_per_step": layer_weights,
                    "weight_searches_per_step": searches,
                    "input_sets_rotated": n_sets, "schedule": schedule,
+                   "search_streams": len(search_sts),
                    "timed_steps_with_events": steps_timed},
         "weight_searches_per_s": searches / (ms_per_step * 1e-3),
         "roofline": roofline,

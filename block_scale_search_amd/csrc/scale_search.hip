@@ -35,6 +35,49 @@ __device__ __forceinline__ void load_group(const uint8_t* __restrict__ p, float 
     }
 }
 
+// A group's raw bytes: two (bf16) or four (f32) 16-byte units, and their 16 weights.
+template <bool BF16>
+constexpr int kGroupUnits = BF16 ? 2 : 4;
+
+template <bool BF16>
+__device__ __forceinline__ void unpack_group(const uint4 (&a)[kGroupUnits<BF16>], float (&w)[16]) {
+    if constexpr (BF16) {
+        const uint32_t d[8] = {a[0].x, a[0].y, a[0].z, a[0].w, a[1].x, a[1].y, a[1].z, a[1].w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            w[2 * i] = bf16_lo(d[i]);
+            w[2 * i + 1] = bf16_hi(d[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[4 * i] = __uint_as_float(a[i].x);
+            w[4 * i + 1] = __uint_as_float(a[i].y);
+            w[4 * i + 2] = __uint_as_float(a[i].z);
+            w[4 * i + 3] = __uint_as_float(a[i].w);
+        }
+    }
+}
+
+// The 16 h values of group g of a row (zeros when not needed or not valid).
+template <bool NEED_H>
+__device__ __forceinline__ void load_h(const float* __restrict__ hm, bool valid, uint32_t g,
+                                       float (&h)[16]) {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) h[j] = 0.0f;
+    if (NEED_H && valid) {
+        const float4* hp = reinterpret_cast<const float4*>(hm + (int64_t)g * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = hp[i];
+            h[4 * i] = v.x;
+            h[4 * i + 1] = v.y;
+            h[4 * i + 2] = v.z;
+            h[4 * i + 3] = v.w;
+        }
+    }
+}
+
 // One lane's group: its 16 weights and, when a rule needs them, its 16 h values.
 template <bool BF16, bool NEED_H>
 __device__ __forceinline__ void load_inputs(const uint8_t* __restrict__ Wm, int64_t ldw_bytes,
@@ -164,9 +207,10 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
 // Exhaustive mode (every code 1..126): the three phases of search_device.h's exhaustive search.
 // Phase 1 per lane (centre block, pending block counts), phase 2 the wave's pending 8-code
 // blocks dealt over its lanes, phase 3 each lane's result from its LDS slot, then the output.
-// The weights and h of a group are read again where phase 2 or the output needs them instead of
-// being held in registers through the kernel, which keeps the register count (and the waves per
-// SIMD) of the windowed kernel.
+// Each lane keeps its group's raw bytes in LDS from phase 1 on, and h is read again from memory
+// (a few KB per matrix, always cached), so that phase 2 (another lane's group) and the output
+// need no registers held through the kernel (the register count, and the waves per SIMD, stay
+// those of the windowed kernel) and W is read from HBM once.
 template <bool BF16, bool WMSE>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
@@ -176,6 +220,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     __shared__ int flag;
     __shared__ int first_item[kSearchThreads];             // per wave: exclusive prefix of counts
     __shared__ unsigned long long slot[kSearchThreads];    // per lane: min (loss, code) key
+    constexpr int U = kGroupUnits<BF16>;
+    __shared__ uint4 wraw[kSearchThreads * U];              // per lane: its group's raw bytes
     const int64_t batch = blockIdx.y;
     const uint32_t gpr = in >> 4;
     const uint32_t G = out * gpr;
@@ -193,8 +239,16 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     {
         const uint32_t row = valid ? div_gpr(gi, gpr_magic, gpr_shift) : 0u;
         const uint32_t g = valid ? gi - row * gpr : 0u;
+        uint4 a[U];
+        const uint4* src = reinterpret_cast<const uint4*>(Wm + (int64_t)row * ldw_bytes +
+                                                          (int64_t)g * (BF16 ? 32 : 64));
+#pragma unroll
+        for (int k = 0; k < U; ++k) a[k] = valid ? src[k] : make_uint4(0u, 0u, 0u, 0u);
         float w[16], h[16];
-        load_inputs<BF16, WMSE>(Wm, ldw_bytes, hm, valid, row, g, w, h);
+        load_h<WMSE>(hm, valid, g, h);
+#pragma unroll
+        for (int k = 0; k < U; ++k) wraw[threadIdx.x * U + k] = a[k];
+        unpack_group<BF16>(a, w);
         const bool octave_ok = build_table(S, tab, &flag);
         b = base_code(w, S);
         live = valid && b > 0;
@@ -237,8 +291,12 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         const bool ovalid = has && ogi < G;
         const uint32_t orow = ovalid ? div_gpr(ogi, gpr_magic, gpr_shift) : 0u;
         const uint32_t og = ovalid ? ogi - orow * gpr : 0u;
+        uint4 a[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) a[q] = wraw[(wave0 + owner) * U + q];
         float w[16], h[16];
-        load_inputs<BF16, WMSE>(Wm, ldw_bytes, hm, ovalid, orow, og, w, h);
+        unpack_group<BF16>(a, w);
+        load_h<WMSE>(hm, ovalid, og, h);
         float bl = __builtin_inff();
         int cl = 255;
         scan8<WMSE>(w, h, tab, first, bl, cl);
@@ -255,10 +313,11 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         best_c = 0;
     }
     if (valid) {
-        const uint32_t row = div_gpr(gi, gpr_magic, gpr_shift);
-        const uint32_t g = gi - row * gpr;
-        float w[16], h[16];
-        load_inputs<BF16, false>(Wm, ldw_bytes, hm, true, row, g, w, h);
+        uint4 a[U];
+#pragma unroll
+        for (int q = 0; q < U; ++q) a[q] = wraw[threadIdx.x * U + q];
+        float w[16];
+        unpack_group<BF16>(a, w);
         emit_group(w, tab, best_c, best, live ? best_c - b : 0, batch * (int64_t)G + gi, o);
     }
 }

@@ -3,9 +3,10 @@
 For each synthetic layer (8B attention, 8B MLP down, 128-expert MoE batch, both 70B MLP shapes,
 and the proposal-centred variant on the 70B up shape):
   - h from the GPU, computed by the calls the benchmark makes (one layer-statistics call for
-    one token chunk, deferred token chunks plus one finalize for the chunked 70B layers, the
+    one token chunk, one call over all resident token chunks for the chunked 70B layers, the
     batched call for the MoE batch), against the oracle's h on every column (1e-5 relative;
-    the binary64 sums within 1e-12);
+    the binary64 sums within 1e-12); for the chunked layers the deferred form (one call per
+    chunk, one finalize) too;
   - the global scale S against the oracle's, exactly;
   - every mode of the workload, one test per mode, on the whole matrix: the GPU's search with
     its own h against the oracle's with the oracle's h. When the two h agree bit for bit (the
@@ -75,19 +76,27 @@ def _layer(nv, name):
         acc_o, h_o = oracle.diag_hessian(host_w(X))
         del X
     else:
-        # token chunks of one calibration set: deferred partial sums, one finalize
+        # token chunks of one calibration set, all resident: one partial launch over every
+        # chunk and one finalize (the benchmark's call); the deferred form (one partial call
+        # per chunk, one finalize) is checked against the oracle as well
         T0 = cfg.chunk_tokens
-        ws = torch.empty(nv.nvfp4_diag_hessian_workspace_size(T0, n, 1), dtype=torch.uint8,
-                         device=DEV)
-        for c in range(workloads.n_chunks(cfg)):
-            X, _ = workloads.make_activation_chunk(cfg, sigma, c, DEV)
-            nv.nvfp4_diag_hessian(X, X.shape[0], n, n, None, None, c > 0, ws)
-            torch.cuda.synchronize()
+        chunks = [workloads.make_activation_chunk(cfg, sigma, c, DEV)[0]
+                  for c in range(workloads.n_chunks(cfg))]
+        for X in chunks:
             acc_o, h_o = oracle.diag_hessian(host_w(X), acc_o)
-            del X
+        ws = torch.empty(max(nv.nvfp4_diag_hessian_chunks_workspace_size(
+            [X.shape[0] for X in chunks], n), nv.nvfp4_diag_hessian_workspace_size(T0, n, 1)),
+            dtype=torch.uint8, device=DEV)
+        acc_d = torch.empty(n, dtype=torch.float64, device=DEV)
+        for c, X in enumerate(chunks):
+            nv.nvfp4_diag_hessian(X, X.shape[0], n, n, None, None, c > 0, ws)
+        nv.nvfp4_diag_hessian_finalize(torch.bfloat16, T0, n, acc_d, None, False, ws)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(acc_d.cpu().numpy(), acc_o, rtol=1e-12, atol=0)
         acc_g = torch.empty(n, dtype=torch.float64, device=DEV)
         h_g = torch.empty(n, dtype=torch.float32, device=DEV)
-        nv.nvfp4_diag_hessian_finalize(torch.bfloat16, T0, n, acc_g, h_g, False, ws)
+        nv.nvfp4_diag_hessian_chunks(chunks, n, n, acc_g, h_g, False, ws)
+        del chunks
         S = nv.global_scale(W, rule)
     torch.cuda.synchronize()
     np.testing.assert_allclose(acc_g.cpu().numpy().reshape(acc_o.shape), acc_o, rtol=1e-12, atol=0)
