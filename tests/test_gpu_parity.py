@@ -83,9 +83,10 @@ def test_padded_rows_and_strided_batch(nv):
     h = _h(256, seed=6, batch=2)
     S = nv.global_scale(view, nv.GS_AMAX_448)
     assert torch.equal(S, nv.global_scale(base.contiguous(), nv.GS_AMAX_448))
-    g = gpu_search(nv, view, h, S, "wmse", -9, 6, False)
-    o = oracle_search(base, h.cpu().numpy(), S.cpu().numpy(), "wmse", -9, 6, False)
-    assert_same(g, o, "strided")
+    for lo, hi, exh in ((-9, 6, False), (0, 0, True)):
+        g = gpu_search(nv, view, h, S, "wmse", lo, hi, exh)
+        o = oracle_search(base, h.cpu().numpy(), S.cpu().numpy(), "wmse", lo, hi, exh)
+        assert_same(g, o, f"strided exh={exh}")
 
 
 @pytest.mark.parametrize("window", [(-9, 6), (-3, 7), (0, 0), (-1, 0), (0, 5), (-125, 125),
@@ -423,6 +424,7 @@ def test_hessian_deferred_ragged_chunks(nv, inp, sizes, ws_tokens):
     (1040, [3000, 0, 17, 1234, 1], 1040),       # ragged sizes, an empty chunk
     (640, [2500, 700], 704),                     # padded rows
     (24, [1], 24),                               # one chunk of one token
+    (512, [37 * (i % 5) + 1 for i in range(64)], 512),   # the largest chunk count, 64
 ])
 def test_hessian_chunks_one_launch(nv, dtype, inp, sizes, ldx):
     """Chunks at separate addresses in one partial launch and one finalize: h over all their
