@@ -5,8 +5,10 @@ One step = the whole path over one synthetic layer held in HBM, or over both mat
   diagonal Hessian over its X (8192-token chunks: deferred partial sums plus one finalize; one
   chunk: one call that also computes the global scale) -> global scale of W -> scale search +
   pack for every mode of the workload (mlp70b: WMSE [-9,6] and the exhaustive 126-code mode).
-Two windowed modes of 11 or 16 codes on bf16 W run as one nvfp4_scale_search_rules call (one
-paired launch reads each group once for both); --separate-searches times one call per mode.
+Two modes run as one nvfp4_scale_search_rules call and one launch where the library fuses them:
+a 16-code window with the exhaustive mode of its objective (the window is the exhaustive
+search's first block of codes), or two windows of 11 or 16 codes on bf16 W (one read of each
+group for both); --separate-searches times one call per mode.
 Consecutive layers follow one another as in a model (--schedule pipeline, the default): layer
 j + 1's h and S calls (HBM-bound) run on a second stream while layer j's searches (VALU-bound)
 run on the main stream; every layer still does all of its work, and an input set's next h and
@@ -17,13 +19,15 @@ priority. Several input sets rotate, so that every step reads its inputs from HB
 Prints one JSON line. `value` is layer weights per second: the weights of the step's matrices
 over the step time (each weight is searched once per mode; `weight_searches_per_s` counts those).
 Per-call times come from HIP events recorded on the launch stream around each library call on
-every 8th timed step (--events-every). The roofline entry is the fixed-work search kernel with
-the largest share of the step: the method's flops per launch (multiply, residual fma, weighting
-multiply and accumulating fma per element and candidate) over its average launch time, against
-the published 157.3 TFLOP/s fp32 vector peak; the lane-issue fraction and the HBM fraction sit
-beside it. The exhaustive mode prunes provable losers, so its work is not fixed; its
-126-code-equivalent rate is reported separately. `traffic` is read from the committed rocprofv3
-counter summary while its kernel-source hash matches the current sources, else null.
+every 8th timed step (--events-every). The roofline entry is the search call with the largest
+share of the step: its flops per launch (multiply, residual fma, weighting multiply and
+accumulating fma per element and candidate scored) over its average launch time, against the
+published 157.3 TFLOP/s fp32 vector peak; the lane-issue fraction and the HBM fraction sit
+beside it. A window scores every candidate; the exhaustive mode skips the codes its lower
+bounds prove to lose, so its candidates are counted on the same inputs with
+nvfp4_scale_search_scored (outside the timing), and its 126-code-equivalent rate is given too.
+`traffic` is read from the committed rocprofv3 counter summary while its kernel-source hash
+matches the current sources, else null.
 After the timed steps, the pack-at-given-scales entry point, each layer's h stage and each
 search call are timed again on their own, back to back over the input sets.
 
@@ -84,15 +88,48 @@ def is_bf16(cfg) -> bool:
     return str(cfg.w_dtype).endswith("bfloat16")
 
 
+def fused_modes(cfg):
+    """A 16-code window and the exhaustive mode of the same objective, which one
+    nvfp4_scale_search_rules call runs as one launch (the exhaustive search's first block is the
+    window), else None."""
+    for w in cfg.modes:
+        if w.proposal or w.exhaustive or n_candidates(w) != 16:
+            continue
+        for e in cfg.modes:
+            if e.exhaustive and e.objective == w.objective:
+                return [w, e]
+    return None
+
+
 def paired_modes(cfg):
-    """The two windowed modes that run as one nvfp4_scale_search_rules call with a paired
-    launch (bf16 W, exactly two plain windows of 11 or 16 codes), else None."""
+    """The two modes that run as one nvfp4_scale_search_rules call and one launch: a 16-code
+    window with the exhaustive mode of its objective (fused launch), or exactly two plain
+    windows of 11 or 16 codes on bf16 W (paired launch); else None."""
+    fused = fused_modes(cfg)
+    if fused is not None:
+        return fused
     plain = [m for m in cfg.modes if not m.proposal]
     if len(plain) != 2 or len(plain) != len(cfg.modes) or not is_bf16(cfg):
         return None
     if any(m.exhaustive or n_candidates(m) not in (11, 16) for m in plain):
         return None
     return plain
+
+
+def kernel_name(cfg, label: str) -> str:
+    modes = label_modes(cfg, label)
+    what = base_label(label)[len("search:"):]
+    if any(m.exhaustive for m in modes):
+        return f"k_scale_search_exhaustive {what}" + (" (one fused launch)" if len(modes) > 1
+                                                      else "")
+    return f"k_scale_search_pair {what}" if len(modes) > 1 else f"k_scale_search {what}"
+
+
+def centre_lo(cfg, label: str) -> int:
+    """Offset of the exhaustive search's first 16-code block: the fused window's lo, else -8."""
+    modes = label_modes(cfg, label)
+    win = [m for m in modes if not m.exhaustive]
+    return win[0].lo if len(modes) > 1 and win else -8
 
 
 def pair_label(modes) -> str:
@@ -114,11 +151,24 @@ def label_modes(cfg, label: str):
     return pair if pair is not None and label == pair_label(pair) else []
 
 
-def search_work(cfg, label: str):
-    """(flops, lane-operations) a search call needs by the method's definition."""
+def search_work(cfg, label: str, scored=None):
+    """(flops, lane-operations) of a search call. A windowed mode scores every candidate of its
+    window for every weight, by the method's definition. The exhaustive mode skips the codes
+    that a lower bound proves to lose, so its work is the number of (group, code) candidates it
+    scores on the call's inputs (`scored`, from nvfp4_scale_search_scored), times 16 elements;
+    a 16-code window fused with it is its first block, so it adds nothing."""
     modes = label_modes(cfg, label)
-    flops = sum(cfg.n_weights * n_candidates(m) * FLOPS_PER_ELEM_CAND[m.objective] for m in modes)
-    ops = sum(cfg.n_weights * n_candidates(m) * OPS_PER_ELEM_CAND[m.objective] for m in modes)
+    flops = ops = 0
+    exh = [m for m in modes if m.exhaustive]
+    for m in modes:
+        if m.exhaustive:
+            n_ec = scored * 16
+        elif exh:
+            continue
+        else:
+            n_ec = cfg.n_weights * n_candidates(m)
+        flops += n_ec * FLOPS_PER_ELEM_CAND[m.objective]
+        ops += n_ec * OPS_PER_ELEM_CAND[m.objective]
     return flops, ops
 
 
@@ -288,11 +338,13 @@ class Kind:
                 "stage"))
         pair = None if self.separate_searches else paired_modes(cfg)
         if pair is not None:
-            # two windowed rules in one call: one launch reads each group once for both
+            # two rules in one call and one launch: two windows read each group once for both,
+            # or a 16-code window is the exhaustive search's first block
             idx = [cfg.modes.index(m) for m in pair]
             wm_any = any(m.objective == "wmse" for m in pair)
             rules = [dict(objective=nv.WMSE if m.objective == "wmse" else nv.MSE, lo=m.lo,
-                          hi=m.hi, exhaustive=False, scales=s.scales[i], packed=s.packed[i])
+                          hi=m.hi, exhaustive=m.exhaustive, scales=s.scales[i],
+                          packed=s.packed[i])
                      for m, i in zip(pair, idx)]
             out.append((pair_label(pair), nv.nvfp4_scale_search_rules(
                 s.W, b, o, n, ldw, sw, 16, s.h if wm_any else None, n if wm_any else 0, s.S,
@@ -667,16 +719,36 @@ def main():
         return p0.elapsed_time(p1) * 1e3 / reps
 
     nv = kinds[0].nv
+    kind_of = {}
+    for kd in kinds:
+        for lab, _, _ in layer_calls[kinds.index(kd)][0]:
+            kind_of[lab] = kd
+    # the work of each search call with an exhaustive mode: the candidates it scores on each
+    # input set (every set's h and S made again first, outside the timing; same values)
+    alone_calls = [[kd.calls(s) for s in kd.sets] for kd in kinds]   # all on the main stream
+    for r in range(R):
+        for calls in alone_calls[r]:
+            for _, f, role in calls:
+                if role == "stage":
+                    f()
+    torch.cuda.synchronize()
+    scored = {}
+    for lab in dict.fromkeys(l for l in step_labels if base_label(l).startswith("search")):
+        kd = kind_of[lab]
+        e = next((m for m in label_modes(kd.cfg, lab) if m.exhaustive), None)
+        if e is None:
+            continue
+        wm = e.objective == "wmse"
+        counts = [nv.scale_search_scored(s.W, s.h if wm else None, s.S,
+                                         nv.WMSE if wm else nv.MSE, centre_lo(kd.cfg, lab))
+                  for s in kd.sets]
+        scored[lab] = sum(counts) / len(counts)
     kernels = {}
     per_label = {}
     for i in sorted(rows):
         for lab, e0, e1 in rows[i]:
             per_label.setdefault(lab, []).append(e0.elapsed_time(e1) * 1e3)  # us
     steps_timed = len(rows)
-    kind_of = {}
-    for kd in kinds:
-        for lab, _, _ in layer_calls[kinds.index(kd)][0]:
-            kind_of[lab] = kd
     for lab, us in per_label.items():
         cfg = kind_of[lab].cfg
         per_step = step_labels.count(lab)
@@ -687,15 +759,17 @@ def main():
              "frac_hbm": round(nb / us_avg / 1e3 / HBM_PEAK_GBS, 4)}
         if base_label(lab).startswith("search"):
             k["weights/s"] = cfg.n_weights / (us_avg * 1e-6)
-            nf, no = search_work(cfg, lab)
-            if "exhaustive" in lab:
-                # exact pruning skips candidates that provably lose, so the 126-candidate flop
-                # count over the time is an equivalent rate, not a roofline figure
-                k["TFLOP/s_126_equivalent"] = round(nf / us_avg / 1e6, 2)
-            else:
-                k["TFLOP/s"] = round(nf / us_avg / 1e6, 2)
-                k["frac_157.3_TFLOP/s"] = round(nf / us_avg / 1e6 / VALU_PUBLISHED_TFLOPS, 4)
-                k["frac_valu_issue"] = round(no / us_avg / 1e6 / VALU_ISSUE_TOPS, 4)
+            nf, no = search_work(cfg, lab, scored.get(lab))
+            k["TFLOP/s"] = round(nf / us_avg / 1e6, 2)
+            k["frac_157.3_TFLOP/s"] = round(nf / us_avg / 1e6 / VALU_PUBLISHED_TFLOPS, 4)
+            k["frac_valu_issue"] = round(no / us_avg / 1e6 / VALU_ISSUE_TOPS, 4)
+            if lab in scored:
+                groups = cfg.n_weights // 16
+                k["scored_codes_per_group"] = round(scored[lab] / groups, 3)
+                # every one of the 126 codes counted, as an unpruned search would score them
+                e = next(m for m in label_modes(cfg, lab) if m.exhaustive)
+                k["TFLOP/s_126_equivalent"] = round(
+                    groups * 126 * 16 * FLOPS_PER_ELEM_CAND[e.objective] / us_avg / 1e6, 2)
         kernels[lab] = k
 
     # the h stage of each matrix in the step: all chunk calls plus the finalize (or the one
@@ -744,7 +818,6 @@ def main():
             "GB/s": round(pack_bytes / pack_us / 1e3, 1),
             "frac_hbm": round(pack_bytes / pack_us / 1e3 / HBM_PEAK_GBS, 4)}
     search_alone = {}
-    alone_calls = [[kd.calls(s) for s in kd.sets] for kd in kinds]   # all on the main stream
     for lab in dict.fromkeys(l for l in step_labels if base_label(l).startswith("search")):
         fs = [f for r in range(R) for calls in alone_calls[r] for l, f, _ in calls if l == lab]
         search_alone[lab] = back_to_back(fs, max(4, 3 * len(fs)))
@@ -757,7 +830,7 @@ def main():
         g = groups.setdefault(base_label(lab), {"labels": [], "us": 0.0, "flops": 0, "ops": 0,
                                                 "bytes": 0, "launches": 0, "alone_us": 0.0})
         cfg = kind_of[lab].cfg
-        nf, no = search_work(cfg, lab)
+        nf, no = search_work(cfg, lab, scored.get(lab))
         n_per = step_labels.count(lab)
         g["labels"].append(lab)
         g["us"] += kernels[lab]["avg_us"] * n_per
@@ -766,20 +839,28 @@ def main():
         g["bytes"] += algorithmic_bytes(cfg, lab) * n_per
         g["launches"] += n_per
         g["alone_us"] += search_alone[lab] * n_per
-    fixed = {k: v for k, v in groups.items() if "exhaustive" not in k}
-    dom = max(fixed, key=lambda k: fixed[k]["us"])
-    g = fixed[dom]
+    # the search call (same mode or modes over every matrix of the step) with the largest share
+    # of the step
+    dom = max(groups, key=lambda k: groups[k]["us"])
+    g = groups[dom]
     us_launch = g["us"] / g["launches"]
     achieved = g["flops"] / g["us"] / 1e6
+    dom_kd = kind_of[g["labels"][0]]
+    pruned = any(m.exhaustive for m in label_modes(dom_kd.cfg, g["labels"][0]))
     roofline = {
-        "bound": "alu", "kernel": f"k_scale_search {dom[len('search:'):]}"
-        if "+" not in dom else f"k_scale_search_pair {dom[len('search:'):]}",
+        "bound": "alu", "kernel": kernel_name(dom_kd.cfg, g["labels"][0]),
         "achieved": round(achieved, 2), "peak": VALU_PUBLISHED_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / VALU_PUBLISHED_TFLOPS, 4),
         "traffic": read_traffic(args.workload, dom),
         "alg_flops_per_launch": g["flops"] // g["launches"],
         "avg_launch_us": round(us_launch, 3), "launches_per_step": g["launches"],
         "flops_per_element_candidate": FLOPS_PER_ELEM_CAND,
+        "flops_counted": ("element-candidates the exhaustive search scores (its first block of "
+                          "16 codes, which is the fused window, plus every block of 8 that its "
+                          "exact lower bounds keep; nvfp4_scale_search_scored on the same "
+                          "inputs), x flops per element-candidate" if pruned else
+                          "every candidate of the window for every weight, x flops per "
+                          "element-candidate"),
         "share_of_step": round(g["us"] / (ms_per_step * 1e3), 4),
         "lane_issue": {"achieved": round(g["ops"] / g["us"] / 1e6, 2), "peak": VALU_ISSUE_TOPS,
                        "unit": "T lane-operations/s",
@@ -796,17 +877,22 @@ def main():
                   "note": "the same calls back to back outside the timed steps; in the steps "
                           "they share the compute units with the next layer's h and S"},
     }
+    if pruned:
+        groups_per_launch = sum(kind_of[l].cfg.n_weights // 16 * step_labels.count(l)
+                                for l in g["labels"]) / g["launches"]
+        e = next(m for m in label_modes(dom_kd.cfg, g["labels"][0]) if m.exhaustive)
+        eq = groups_per_launch * 126 * 16 * FLOPS_PER_ELEM_CAND[e.objective]
+        roofline["scored_codes_per_group"] = round(
+            sum(scored[l] * step_labels.count(l) for l in g["labels"]) / g["launches"]
+            / groups_per_launch, 3)
+        roofline["TFLOP/s_126_equivalent"] = round(eq / us_launch / 1e6, 2)
     others = {k: v for k, v in groups.items() if k != dom}
     if others:
         roofline["other_searches"] = {
             k: {"us_per_step": round(v["us"], 2),
                 "share_of_step": round(v["us"] / (ms_per_step * 1e3), 4),
-                **({"TFLOP/s_126_equivalent": round(v["flops"] / v["us"] / 1e6, 2),
-                    "note": "exact pruning skips provably losing codes, so the work is not "
-                            "fixed; 126 codes per group counted"}
-                   if "exhaustive" in k else
-                   {"TFLOP/s": round(v["flops"] / v["us"] / 1e6, 2),
-                    "frac": round(v["flops"] / v["us"] / 1e6 / VALU_PUBLISHED_TFLOPS, 4)})}
+                "TFLOP/s": round(v["flops"] / v["us"] / 1e6, 2),
+                "frac": round(v["flops"] / v["us"] / 1e6 / VALU_PUBLISHED_TFLOPS, 4)}
             for k, v in others.items()}
 
     extras = run_extras(args, kinds[0], dev, p0, p1, main_st, back_to_back)

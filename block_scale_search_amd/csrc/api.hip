@@ -270,6 +270,30 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
         offset, nullptr, nullptr, static_cast<hipStream_t>(stream)));
 }
 
+nvfp4_status nvfp4_scale_search_scored(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                       int64_t in, int64_t ldw, int64_t stride_w,
+                                       int32_t group_size, const float* h, int64_t stride_h,
+                                       int objective, int32_t centre_lo, const float* S,
+                                       uint64_t* count, void* stream) {
+    if (group_size != 16) return NVFP4_ERR_ARG;
+    if (objective != NVFP4_MSE && objective != NVFP4_WMSE) return NVFP4_ERR_ARG;
+    if (centre_lo < -15 || centre_lo > 0) return NVFP4_ERR_WINDOW;
+    nvfp4_status st = check_weights(W, w_dtype, batch, out, in, ldw, stride_w);
+    if (st != NVFP4_OK) return st;
+    const bool wmse = objective == NVFP4_WMSE;
+    if (wmse) {
+        if (stride_h < 0 || (batch > 1 && stride_h < in) || stride_h % 4 != 0) return NVFP4_ERR_SHAPE;
+    }
+    if (batch == 0 || out == 0 || in == 0) return NVFP4_OK;
+    if (S == nullptr || count == nullptr) return NVFP4_ERR_NULL;
+    if (wmse && h == nullptr) return NVFP4_ERR_NULL;
+    if ((reinterpret_cast<uintptr_t>(S) & 3u) || !aligned8(count) || (wmse && !aligned16(h)))
+        return NVFP4_ERR_ALIGN;
+    return hip_status(nvfp4::launch_exhaustive_scored(
+        W, w_dtype == NVFP4_DTYPE_BF16, batch, out, in, ldw, stride_w, wmse ? h : nullptr,
+        wmse ? stride_h : 0, wmse, centre_lo, S, count, static_cast<hipStream_t>(stream)));
+}
+
 nvfp4_status nvfp4_scale_search_rules(const void* W, int w_dtype, int64_t batch, int64_t out,
                                       int64_t in, int64_t ldw, int64_t stride_w,
                                       int32_t group_size, const float* h, int64_t stride_h,

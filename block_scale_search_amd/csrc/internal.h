@@ -107,6 +107,12 @@ hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, in
                                      int64_t stride_h, const float* S, const SearchRule* rules,
                                      int n_rules, hipStream_t stream);
 
+// Work count of the exhaustive search (candidates scored), added to *count.
+hipError_t launch_exhaustive_scored(const void* W, bool bf16, int64_t batch, int64_t out,
+                                   int64_t in, int64_t ldw, int64_t stride_w, const float* h,
+                                   int64_t stride_h, bool wmse, int clo, const float* S,
+                                   uint64_t* count, hipStream_t stream);
+
 // Layer-output error: workspace bytes (residual halves + token-tile partials) and launch.
 size_t output_error_workspace_bytes(int64_t tokens, int64_t out, int64_t in);
 int64_t output_error_tiles(int64_t tokens, int64_t out);   // GEMM workgroups

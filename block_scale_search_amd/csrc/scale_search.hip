@@ -211,11 +211,17 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
 // (a few KB per matrix, always cached), so that phase 2 (another lane's group) and the output
 // need no registers held through the kernel (the register count, and the waves per SIMD, stay
 // those of the windowed kernel) and W is read from HBM once.
-template <bool BF16, bool WMSE>
+// WIN: a 16-code window wlo .. wlo + 15 under the same objective is searched in the same pass.
+// The centre block is then placed on the window (codes b + wlo ..), so wherever the window is
+// unclipped and normal its ascending scan is the centre block's, and the window's outputs
+// (written to ow) come from losses the exhaustive search computes anyway; a lane whose window
+// is clipped or reaches the subnormal codes scans its window codes on their own. Without WIN
+// the centre block is codes b - 8 .. b + 7.
+template <bool BF16, bool WMSE, bool WIN>
 __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
     uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec,
-    int64_t stride_h, const float* __restrict__ S_arr, RuleOut o) {
+    int64_t stride_h, const float* __restrict__ S_arr, RuleOut o, int wlo, RuleOut ow) {
     __shared__ float2 tab[128];
     __shared__ int flag;
     __shared__ int first_item[kSearchThreads];             // per wave: exclusive prefix of counts
@@ -252,12 +258,33 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         const bool octave_ok = build_table(S, tab, &flag);
         b = base_code(w, S);
         live = valid && b > 0;
-        // +inf with code 1: a group whose every loss overflows keeps code 1, as the ascending
-        // scan does
         float best = __builtin_inff();
         int best_c = 1;
-        if (__any(live))
-            exhaustive_centre<WMSE>(w, h, tab, octave_ok, live, b, best, best_c, c0, n_up, n_dn);
+        if (__any(live)) {
+            c0 = centre_scan<WMSE>(w, h, tab, octave_ok, live, b, WIN ? wlo : -8, best, best_c);
+            if constexpr (WIN) {
+                float wb = best;
+                int wc = best_c;
+                const bool own = live && c0 != b + wlo;
+                if (__any(own)) {
+                    // the window's codes clamp(b + wlo + p, 1, 126), p = 0..15, ascending
+                    float wb2 = __builtin_inff();
+                    int wc2 = min(max(b + wlo, 1), 126);
+                    search_window<WMSE, 0>(w, h, tab, false, own, b + wlo, 16, wb2, wc2);
+                    wb = own ? wb2 : wb;
+                    wc = own ? wc2 : wc;
+                }
+                if (valid)
+                    emit_group(w, tab, live ? wc : 0, live ? wb : 0.0f, live ? wc - b : 0,
+                               batch * (int64_t)G + gi, ow);
+            }
+            pending_blocks<WMSE>(w, h, tab, live, c0, best, n_up, n_dn);
+            // +inf with code 1: a group whose every loss overflows keeps code 1, as the
+            // ascending scan over all codes does
+            if (!(best < __builtin_inff())) best_c = 1;
+        } else if constexpr (WIN) {
+            if (valid) emit_group(w, tab, 0, 0.0f, 0, batch * (int64_t)G + gi, ow);
+        }
         slot[threadIdx.x] = loss_key(best, best_c);
     }
 
@@ -319,6 +346,54 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         float w[16];
         unpack_group<BF16>(a, w);
         emit_group(w, tab, best_c, best, live ? best_c - b : 0, batch * (int64_t)G + gi, o);
+    }
+}
+
+// Work count of the exhaustive search on the same inputs: per group with a nonzero base code,
+// the 16 codes of its centre block (centre offset clo) and the codes 1..126 of every pending
+// block that its lower bounds keep, summed over the launch and added to *count. It runs the
+// exhaustive kernel's phase-1 code, so the decisions are the same.
+template <bool BF16, bool WMSE>
+__global__ __launch_bounds__(kSearchThreads) void k_exhaustive_scored(
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
+    uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec,
+    int64_t stride_h, const float* __restrict__ S_arr, int clo,
+    unsigned long long* __restrict__ count) {
+    __shared__ float2 tab[128];
+    __shared__ int flag;
+    __shared__ uint32_t wsum[kSearchThreads / 64];
+    const int64_t batch = blockIdx.y;
+    const uint32_t gpr = in >> 4;
+    const uint32_t G = out * gpr;
+    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
+    const bool valid = gi < G;
+    const uint32_t row = valid ? div_gpr(gi, gpr_magic, gpr_shift) : 0u;
+    const uint32_t g = valid ? gi - row * gpr : 0u;
+    float w[16], h[16];
+    load_inputs<BF16, WMSE>(W + batch * stride_w_bytes, ldw_bytes, hvec + batch * stride_h, valid,
+                            row, g, w, h);
+    const float S = S_arr[batch];
+    const bool octave_ok = build_table(S, tab, &flag);
+    const int b = base_code(w, S);
+    const bool live = valid && b > 0;
+    uint32_t n = 0;
+    if (__any(live)) {
+        float best;
+        int best_c, n_up, n_dn;
+        const int c0 = centre_scan<WMSE>(w, h, tab, octave_ok, live, b, clo, best, best_c);
+        pending_blocks<WMSE>(w, h, tab, live, c0, best, n_up, n_dn);
+        const int up = c0 + 16, dn = c0 - 1;
+        if (live) n = 16 + (min(up + 8 * n_up, 127) - up) + min(8 * n_dn, dn);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);
+    if ((threadIdx.x & 63) == 0) wsum[threadIdx.x >> 6] = n;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t t = 0;
+#pragma unroll
+        for (int k = 0; k < kSearchThreads / 64; ++k) t += wsum[k];
+        atomicAdd(count, (unsigned long long)t);
     }
 }
 
@@ -438,6 +513,21 @@ bool pairable(const SearchRule& r) {
     return !r.exhaustive && (n == 11 || n == 16);
 }
 
+// a 16-code window and an exhaustive rule of the same objective, in either order: one pass
+bool fusable(const SearchRule& r, const SearchRule& q) {
+    const SearchRule& win = r.exhaustive ? q : r;
+    const SearchRule& exh = r.exhaustive ? r : q;
+    return exh.exhaustive && !win.exhaustive && win.hi - win.lo + 1 == 16 && win.wmse == exh.wmse;
+}
+
+template <bool B, bool M>
+void launch_fused_t(const SearchArgs& a, const float* S, int wlo, const RuleOut& exh,
+                    const RuleOut& win, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((k_scale_search_exhaustive<B, M, true>), grid, dim3(kSearchThreads), 0,
+                       stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes, a.stride_w_bytes,
+                       a.h, a.stride_h, S, exh, wlo, win);
+}
+
 }  // namespace
 
 hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, int64_t out,
@@ -448,11 +538,12 @@ hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, in
     const int64_t G = out * gpr;
     SearchArgs a{};
     gpr_divisor(gpr, a.magic, a.shift);
+    const int esz = bf16 ? 2 : 4;
     a.W = static_cast<const uint8_t*>(W);
     a.out = (uint32_t)out;
     a.in = (uint32_t)in;
-    a.ldw_bytes = ldw * 2;
-    a.stride_w_bytes = stride_w * 2;
+    a.ldw_bytes = ldw * esz;
+    a.stride_w_bytes = stride_w * esz;
     a.h = h;
     a.stride_h = stride_h;
     const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
@@ -469,6 +560,17 @@ hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, in
             } else {
                 if (na == 16) launch_pair_b<false, 16>(a, S, r, q, grid, stream);
                 else launch_pair_b<false, 11>(a, S, r, q, grid, stream);
+            }
+            i += 2;
+        } else if (i + 1 < n_rules && fusable(r, rules[i + 1])) {
+            const SearchRule& win = r.exhaustive ? rules[i + 1] : r;
+            const SearchRule& exh = r.exhaustive ? r : rules[i + 1];
+            if (bf16) {
+                if (r.wmse) launch_fused_t<true, true>(a, S, win.lo, exh.out, win.out, grid, stream);
+                else launch_fused_t<true, false>(a, S, win.lo, exh.out, win.out, grid, stream);
+            } else {
+                if (r.wmse) launch_fused_t<false, true>(a, S, win.lo, exh.out, win.out, grid, stream);
+                else launch_fused_t<false, false>(a, S, win.lo, exh.out, win.out, grid, stream);
             }
             i += 2;
         } else {
@@ -519,9 +621,9 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
         if (proposal || sfp || src.S == nullptr) return hipErrorInvalidValue;
         const RuleOut o{scales, packed, loss, offset};
 #define NVFP4_EXH(B, M)                                                                        \
-        hipLaunchKernelGGL((k_scale_search_exhaustive<B, M>), grid, dim3(kSearchThreads), 0,   \
-                           stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes,            \
-                           a.stride_w_bytes, a.h, a.stride_h, src.S, o)
+        hipLaunchKernelGGL((k_scale_search_exhaustive<B, M, false>), grid, dim3(kSearchThreads), \
+                           0, stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes,         \
+                           a.stride_w_bytes, a.h, a.stride_h, src.S, o, 0, RuleOut{})
         if (bf16) {
             if (wmse) NVFP4_EXH(true, true); else NVFP4_EXH(true, false);
         } else {
@@ -538,6 +640,31 @@ hipError_t launch_scale_search(const void* W, bool bf16, int64_t batch, int64_t 
         if (wmse) launch_modes<false, true>(a, nwin, proposal, sfp, grid, stream);
         else launch_modes<false, false>(a, nwin, proposal, sfp, grid, stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_exhaustive_scored(const void* W, bool bf16, int64_t batch, int64_t out,
+                                   int64_t in, int64_t ldw, int64_t stride_w, const float* h,
+                                   int64_t stride_h, bool wmse, int clo, const float* S,
+                                   uint64_t* count, hipStream_t stream) {
+    const int64_t gpr = in / 16;
+    const int64_t G = out * gpr;
+    uint64_t magic;
+    uint32_t shift;
+    gpr_divisor(gpr, magic, shift);
+    const int esz = bf16 ? 2 : 4;
+    const dim3 grid((uint32_t)((G + kSearchThreads - 1) / kSearchThreads), (uint32_t)batch);
+    auto* c = reinterpret_cast<unsigned long long*>(count);
+#define NVFP4_SCORED(B, M)                                                                     \
+    hipLaunchKernelGGL((k_exhaustive_scored<B, M>), grid, dim3(kSearchThreads), 0, stream,     \
+                       static_cast<const uint8_t*>(W), (uint32_t)out, (uint32_t)in, magic,    \
+                       shift, ldw * esz, stride_w * esz, h, stride_h, S, clo, c)
+    if (bf16) {
+        if (wmse) NVFP4_SCORED(true, true); else NVFP4_SCORED(true, false);
+    } else {
+        if (wmse) NVFP4_SCORED(false, true); else NVFP4_SCORED(false, false);
+    }
+#undef NVFP4_SCORED
     return hipGetLastError();
 }
 

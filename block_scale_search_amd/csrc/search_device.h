@@ -252,13 +252,37 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
 // the lexicographic minimum of (loss, code) over all 126 codes: the ascending scan's first
 // minimum.
 
-// Phase 1 of one lane: the centre block, then the numbers of 8-code blocks needed above
-// (n_up, from code c0 + 16) and below (n_dn, down from code c0 - 1). c0 is returned too.
+// Phase 1 of one lane, first half: the centre block of 16 codes c0 .. c0 + 15 with
+// c0 = clamp(b + clo, 8, 111) (at least 8 and at most 111 so that octave pairs stay normal),
+// scanned in ascending order from (+inf, c0). Where c0 = b + clo this is exactly the ascending
+// scan of the window clo .. clo + 15, so a 16-code window's result comes from the same losses.
+// Returns c0.
 template <bool WMSE>
-__device__ __forceinline__ void exhaustive_centre(const float (&w)[16], const float (&h)[16],
-                                                  const float2* __restrict__ tab, bool octave_ok,
-                                                  bool live, int b, float& best, int& best_c,
-                                                  int& c0, int& n_up, int& n_dn) {
+__device__ __forceinline__ int centre_scan(const float (&w)[16], const float (&h)[16],
+                                           const float2* __restrict__ tab, bool octave_ok,
+                                           bool live, int b, int clo, float& best,
+                                           int& best_c) {
+    const int c0 = live ? min(max(b + clo, 8), 111) : 8;
+    best = __builtin_inff();
+    best_c = c0;
+    if (octave_ok) {
+        scan_block<WMSE, 16>(w, h, tab + c0, c0, 16, best, best_c);
+    } else {
+        scan8<WMSE>(w, h, tab, c0, best, best_c);
+        scan8<WMSE>(w, h, tab, c0 + 8, best, best_c);
+    }
+    return c0;
+}
+
+// Phase 1, second half: the numbers of 8-code blocks needed above the centre block (n_up, from
+// code c0 + 16) and below it (n_dn, down from code c0 - 1), given the centre's best loss.
+template <bool WMSE>
+__device__ __forceinline__ void pending_blocks(const float (&w)[16], const float (&h)[16],
+                                               const float2* __restrict__ tab, bool live, int c0,
+                                               float best, int& n_up, int& n_dn) {
+    n_up = 0;
+    n_dn = 0;
+    if (!live) return;
     float amax = 0.0f, hmax = 1.0f;
     bool h_ok = true;
 #pragma unroll
@@ -270,18 +294,6 @@ __device__ __forceinline__ void exhaustive_centre(const float (&w)[16], const fl
         }
     }
     const float scale_ref = amax * (1.0f + hmax);
-
-    // centre block: 16 codes from c0 (at least 8 and at most 111 so that pairs stay normal)
-    c0 = live ? min(max(b - 8, 8), 111) : 8;
-    if (octave_ok) {
-        scan_block<WMSE, 16>(w, h, tab + c0, c0, 16, best, best_c);
-    } else {
-        scan8<WMSE>(w, h, tab, c0, best, best_c);
-        scan8<WMSE>(w, h, tab, c0 + 8, best, best_c);
-    }
-    n_up = 0;
-    n_dn = 0;
-    if (!live) return;
     const int up = c0 + 16, dn = c0 - 1;
     const int all_up = up <= 126 ? (126 - up) / 8 + 1 : 0;
     const int all_dn = dn >= 1 ? (dn - 1) / 8 + 1 : 0;

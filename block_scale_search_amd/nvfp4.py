@@ -56,6 +56,8 @@ _SIGS = {
                             _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_scale_search_rules": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _P,
                                   ctypes.POINTER(SearchRule), _I32, _P], _I),
+    "nvfp4_scale_search_scored": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I, _I32,
+                                   _P, _P, _P], _I),
     "nvfp4_scale_search_proposal": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I64, _I,
                                      _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P], _I),
     "nvfp4_pack": ([_P, _I, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P], _I),
@@ -286,6 +288,17 @@ def nvfp4_scale_search_rules(W, batch, out, inp, ldw, stride_w, group_size, h, s
     return None
 
 
+def nvfp4_scale_search_scored(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h,
+                              objective, centre_lo, S, count, stream=None, prepare=False):
+    _need(S, batch, "S")
+    _need(count, 1, "count")
+    return _run("nvfp4_scale_search_scored", (
+        _dev(W, "W", (torch.float32, torch.bfloat16)), _wdtype(W), batch, out, inp, ldw, stride_w,
+        group_size, _dev(h, "h", (torch.float32,)), stride_h, objective, centre_lo,
+        _dev(S, "S", (torch.float32,)), _dev(count, "count", (torch.int64,)), _stream(stream)),
+        prepare)
+
+
 def nvfp4_scale_search_proposal(W, batch, out, inp, ldw, stride_w, group_size, h, stride_h,
                                 objective, lo, hi, center, incoming, S, scales, packed, loss=None,
                                 offset=None, stream=None, prepare=False):
@@ -503,6 +516,23 @@ def scale_search_rules(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor,
     nvfp4_scale_search_rules(W, b, o, n, ldw, sw, 16, h if wmse else None, stride_h, S, specs,
                              stream)
     return outs
+
+
+def scale_search_scored(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objective: int,
+                        centre_lo: int = -8, stream=None) -> int:
+    """Number of (group, code) candidates the exhaustive search scores on these inputs (centre
+    block at base + centre_lo: -8 for scale_search's exhaustive mode, the window's lo when a
+    16-code window and the exhaustive rule share one scale_search_rules launch)."""
+    b, o, n, ldw, sw = _bmat(W)
+    stride_h = 0
+    if objective == WMSE:
+        if h is None:
+            raise ValueError("WMSE needs h")
+        stride_h = h.stride(0) if h.dim() == 2 else 0
+    count = torch.zeros(1, dtype=torch.int64, device=W.device)
+    nvfp4_scale_search_scored(W, b, o, n, ldw, sw, 16, h if objective == WMSE else None, stride_h,
+                              objective, centre_lo, S, count, stream)
+    return int(count.item())
 
 
 def scale_search_proposal(W: torch.Tensor, h: torch.Tensor | None, S: torch.Tensor, objective: int,

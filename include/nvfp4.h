@@ -234,9 +234,16 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
  * and WMSE [-8, 7] windows of one model).
  *
  * rules[k]'s outputs are exactly those of nvfp4_scale_search with that rule's objective, lo, hi,
- * exhaustive and output pointers, and the call's other arguments. Two consecutive windowed rules
- * of 11 or 16 codes on bf16 W run as one launch that reads each group once and shares its
- * table and base code between them; every other rule runs as its own launch.
+ * exhaustive and output pointers, and the call's other arguments. Rules are taken in order,
+ * two at a time where they fit one launch:
+ *   - two consecutive windowed rules of 11 or 16 codes on bf16 W run as one launch that reads
+ *     each group once and shares its table and base code between them;
+ *   - else a windowed rule of 16 codes and an exhaustive rule of the same objective, next to
+ *     each other in either order (bf16 or f32 W), run as one launch: the exhaustive search's
+ *     first block of 16 codes is placed on the window, so the window's losses are the ones the
+ *     exhaustive search computes anyway ([SR] App. D.5: a local window's choice audited
+ *     against the exhaustive optimum over every exportable scale);
+ *   - every other rule runs as its own launch.
  *
  * rules     host, n_rules entries (1 <= n_rules <= 64), read during the call only. The output
  *           buffers of different rules must not overlap.
@@ -260,6 +267,26 @@ nvfp4_status nvfp4_scale_search_rules(const void* W, int w_dtype, int64_t batch,
                                       int32_t group_size, const float* h, int64_t stride_h,
                                       const float* S, const nvfp4_search_rule* rules,
                                       int32_t n_rules, void* stream);
+
+/* ---------------------------------------------------------------------------------------------
+ * Work count of the exhaustive search (for measurement: the exhaustive mode skips every code
+ * whose loss a lower bound proves larger than the best already found, so the codes it scores
+ * depend on the data). Adds to *count the number of (group, code) candidates that the
+ * exhaustive search over these inputs scores: for every group with a nonzero base code, the 16
+ * codes of its first block (codes clamp(base + centre_lo, 8, 111) .. + 15) and the codes 1..126
+ * of every further block of 8 that its bounds do not rule out. It runs the search's own first
+ * phase, so the count is exact for the same W, h and S.
+ *
+ * centre_lo  -8 for nvfp4_scale_search's exhaustive mode; for nvfp4_scale_search_rules' fused
+ *            window + exhaustive launch, the window rule's lo. -15 <= centre_lo <= 0.
+ * count      device, one uint64 (8-byte aligned), added to (not cleared) by the call.
+ * Other arguments as nvfp4_scale_search.
+ * ------------------------------------------------------------------------------------------- */
+nvfp4_status nvfp4_scale_search_scored(const void* W, int w_dtype, int64_t batch, int64_t out,
+                                       int64_t in, int64_t ldw, int64_t stride_w,
+                                       int32_t group_size, const float* h, int64_t stride_h,
+                                       int objective, int32_t centre_lo, const float* S,
+                                       uint64_t* count, void* stream);
 
 /* ---------------------------------------------------------------------------------------------
  * Steps 3-4 with a proposal-centred window and the incoming scale kept on ties ([SR] §4.1.3 and

@@ -95,6 +95,32 @@ def test_scale_search_rejects_bad_arguments(lib):
     assert _search(lib, exh=1, lo=5, hi=-5, W=None) == n.ERR_NULL
 
 
+def _scored(lib, **kw):
+    a = dict(W=FAKE, dt=1, batch=1, out=4, inp=64, ldw=64, sw=256, gs=16, h=FAKE, sh=0, obj=1,
+             clo=-8, S=FAKE, count=FAKE)
+    a.update(kw)
+    return lib.nvfp4_scale_search_scored(a["W"], a["dt"], a["batch"], a["out"], a["inp"],
+                                         a["ldw"], a["sw"], a["gs"], a["h"], a["sh"], a["obj"],
+                                         a["clo"], a["S"], a["count"], None)
+
+
+def test_scale_search_scored_rejects_bad_arguments(lib):
+    from block_scale_search_amd import nvfp4 as n
+    assert _scored(lib, gs=32) == n.ERR_ARG
+    assert _scored(lib, obj=7) == n.ERR_ARG
+    assert _scored(lib, clo=1) == n.ERR_WINDOW
+    assert _scored(lib, clo=-16) == n.ERR_WINDOW
+    assert _scored(lib, dt=5) == n.ERR_DTYPE
+    assert _scored(lib, ldw=32) == n.ERR_SHAPE
+    assert _scored(lib, W=None) == n.ERR_NULL
+    assert _scored(lib, h=None) == n.ERR_NULL                     # WMSE needs h
+    assert _scored(lib, S=None) == n.ERR_NULL
+    assert _scored(lib, count=None) == n.ERR_NULL
+    assert _scored(lib, count=ODD) == n.ERR_ALIGN                 # not 8-byte aligned
+    assert _scored(lib, h=ODD) == n.ERR_ALIGN
+    assert _scored(lib, out=0) == n.OK                             # empty: nothing enqueued
+
+
 def _rules(lib, rules=None, n=None, **kw):
     from block_scale_search_amd import nvfp4 as nv
     a = dict(W=FAKE, dt=1, batch=1, out=4, inp=64, ldw=64, sw=256, gs=16, h=FAKE, sh=0, S=FAKE)

@@ -28,10 +28,33 @@ def test_window_search_work_on_the_70b_matrices():
             n_w * 2 + n_w // 2 + n_w // 16 + cfg.inp * 4
 
 
-def test_exhaustive_counts_126_codes():
+def test_exhaustive_counts_the_codes_it_scores():
+    # the pruned search's work is the (group, code) candidates it scores, 16 elements each
     cfg = C["mlp70b_up"]
-    flops, _ = bench.search_work(cfg, "search:WMSE exhaustive(126)")
-    assert flops == cfg.n_weights * 126 * 6
+    scored = 40 * (cfg.n_weights // 16)
+    flops, ops = bench.search_work(cfg, "search:WMSE exhaustive(126)", scored)
+    assert flops == scored * 16 * 6
+    assert ops == scored * 16 * 5
+    assert bench.centre_lo(cfg, "search:WMSE exhaustive(126)") == -8
+
+
+def test_fused_window_and_exhaustive():
+    # the 70B matrices' two modes are one launch; the window is the exhaustive search's first
+    # block, so the launch's work is the exhaustive search's alone, and both outputs are written
+    for name in ("mlp70b_up", "mlp70b_down", "tiny"):
+        cfg = C[name]
+        pair = bench.paired_modes(cfg)
+        assert [m.label for m in pair] == ["WMSE [-9,6]", "WMSE exhaustive(126)"]
+        label = bench.pair_label(pair)
+        assert bench.centre_lo(cfg, label) == -9
+        assert "k_scale_search_exhaustive" in bench.kernel_name(cfg, label)
+        n_w = cfg.n_weights
+        scored = 33 * (n_w // 16)
+        flops, _ = bench.search_work(cfg, label, scored)
+        assert flops == scored * 16 * 6
+        wb = 2 if bench.is_bf16(cfg) else 4
+        assert bench.algorithmic_bytes(cfg, label) == \
+            n_w * wb + 2 * (n_w // 2 + n_w // 16) + cfg.batch * cfg.inp * 4
 
 
 def test_paired_launch_counts_both_rules():

@@ -14,8 +14,9 @@ and the proposal-centred variant on the 70B up shape):
     bits. Otherwise the GPU's outputs are compared bit for bit with the oracle run on the GPU's
     h, and the fraction of groups whose scale byte differs between the two h (the flip
     fraction) must stay below 1e-4. Both figures are printed for the record.
-The modes that the benchmark runs as one paired launch (attn8b's MSE [-3,7] + WMSE [-8,7]) are
-run here through the same nvfp4_scale_search_rules call.
+The modes that the benchmark runs as one launch (attn8b's MSE [-3,7] + WMSE [-8,7] as a paired
+launch; the 70B matrices' WMSE [-9,6] + exhaustive as one fused launch) are run here through the
+same nvfp4_scale_search_rules call.
 """
 import numpy as np
 import pytest
@@ -32,8 +33,15 @@ _CACHE = {}
 
 
 def _bench_pair(cfg):
-    """The two windowed modes the benchmark runs as one nvfp4_scale_search_rules call (bf16 W,
-    exactly two plain windows of 11 or 16 codes), else None."""
+    """The two modes the benchmark runs as one nvfp4_scale_search_rules call: a 16-code window
+    with the exhaustive mode of its objective (fused launch), or exactly two plain windows of 11
+    or 16 codes on bf16 W (paired launch); else None."""
+    for w in cfg.modes:
+        if w.proposal or w.exhaustive or w.hi - w.lo + 1 != 16:
+            continue
+        for e in cfg.modes:
+            if e.exhaustive and e.objective == w.objective:
+                return [w, e]
     plain = [m for m in cfg.modes if not m.proposal and not m.exhaustive]
     if len(plain) != 2 or len(cfg.modes) != 2 or cfg.w_dtype != torch.bfloat16:
         return None
@@ -134,7 +142,8 @@ def _gpu_outputs(nv, L, mode):
     obj = nv.WMSE if wm else nv.MSE
     pair = _bench_pair(cfg)
     if pair is not None and mode in pair:
-        rules = [(nv.WMSE if m.objective == "wmse" else nv.MSE, m.lo, m.hi, False) for m in pair]
+        rules = [(nv.WMSE if m.objective == "wmse" else nv.MSE, m.lo, m.hi, m.exhaustive)
+                 for m in pair]
         r = nv.scale_search_rules(W, h, S, rules)[pair.index(mode)]
     elif mode.proposal:
         r = nv.scale_search_proposal(W, h if wm else None, S, obj, L["center"], L["incoming"],

@@ -1,6 +1,7 @@
 """GPU parity of nvfp4_scale_search_rules: several rules in one call give, rule by rule, the
 bytes of separate nvfp4_scale_search calls and of the oracle (paired launches for windows of
-11 and 16 codes on bf16 W, single launches for the rest)."""
+11 and 16 codes on bf16 W, one fused launch for a 16-code window next to an exhaustive rule of
+the same objective, single launches for the rest)."""
 import numpy as np
 import pytest
 import torch
@@ -103,3 +104,81 @@ def test_five_rules_two_pairs_and_clipped_windows(nv):
     rules = [(1, -8, 7, False), (0, -3, 7, False), (1, -9, 6, False), (1, -8, 7, False),
              (0, -5, 5, False)]
     _check(nv, W, h, S, rules, "five")
+
+
+def _wide_range(out, inp, dtype, seed):
+    """Rows scaled by 2^0 .. 2^-18 in turn, so that the groups' base codes run over the whole
+    code range: windows clipped at 126, windows inside it, windows reaching the subnormal codes
+    1..7 and clipped at 1."""
+    W, h = _inputs(out, inp, dtype, seed)
+    k = (torch.arange(out, device=DEV) % 19).float()
+    W = (W.float() * torch.exp2(-k)[:, None]).to(dtype)
+    return W, h
+
+
+FUSED = [[(1, -9, 6, False), (1, 0, 0, True)],      # the 70B pair's two modes
+         [(1, 0, 0, True), (1, -8, 7, False)],      # exhaustive rule first
+         [(0, -15, 0, False), (0, 0, 0, True)],     # MSE, window ending at the base code
+         [(0, 0, 15, False), (0, 0, 0, True)]]      # window starting at the base code
+
+
+@pytest.mark.parametrize("rule", ["amax448", "amax256"])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("rules", FUSED, ids=lambda r: "+".join(
+    "exh" if e else f"{o}[{lo},{hi}]" for o, lo, hi, e in r))
+def test_window_and_exhaustive_fused(nv, rules, dtype, rule):
+    """A 16-code window beside an exhaustive rule of the same objective: one launch, whose two
+    outputs equal the separate calls' and the oracle's, over base codes spanning 1..126."""
+    W, h = _wide_range(152, 288, dtype, seed=53)
+    W[0] = 0.0                       # zero groups
+    W[1, :16] = -0.0
+    S = nv.global_scale(W, nv.GS_AMAX_448 if rule == "amax448" else nv.GS_AMAX_256)
+    _check(nv, W, h, S, rules, "fused")
+
+
+def test_fused_overflow_negative_h_and_tiny_scale(nv):
+    """The fused launch where losses overflow, where negative h turns the pruning off, and with
+    a global scale whose lowest codes are subnormal (no octave identity)."""
+    W, h = _inputs(48, 256, torch.float32, seed=55)
+    W[:16] *= 1e4
+    h[:64] = 3e38
+    h[100:140] *= -1.0
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    _check(nv, W, h, S, [(1, -9, 6, False), (1, 0, 0, True)], "fused overflow")
+    Wt, ht = _inputs(32, 128, torch.float32, seed=57)
+    Wt = Wt * 1e-33
+    ht = ht * 1e30
+    St = torch.tensor([2.6e-36], dtype=torch.float32, device=DEV)
+    _check(nv, Wt, ht, St, [(1, -9, 6, False), (1, 0, 0, True)], "fused tiny S")
+    _check(nv, Wt, ht, St, [(0, -8, 7, False), (0, 0, 0, True)], "fused tiny S mse")
+
+
+def test_fused_batched_padded(nv):
+    base, h = _inputs(40, 256, torch.bfloat16, seed=59, batch=3)
+    big = torch.full((3, 48, 320), 7.0, dtype=torch.bfloat16, device=DEV)
+    big[:, :40, :256] = base
+    view = big[:, :40, :256]
+    S = nv.global_scale(view, nv.GS_AMAX_256)
+    _check(nv, view, h, S, [(1, -9, 6, False), (1, 0, 0, True)], "fused batched")
+
+
+def test_scored_count(nv):
+    """The exhaustive search's work count: at least the 16 centre codes and at most all 126 per
+    group with a nonzero base code, all 126 where negative h turns the pruning off, and
+    independent of what else the call runs."""
+    W, h = _wide_range(152, 288, torch.bfloat16, seed=61)
+    W[0] = 0.0
+    S = nv.global_scale(W, nv.GS_AMAX_256)
+    live = int((W.float().view(152, -1, 16).abs().amax(-1) > 0).sum())
+    for obj in (nv.WMSE, nv.MSE):
+        for lo in (-8, -9, 0, -15):
+            n = nv.scale_search_scored(W, h, S, obj, lo)
+            assert 16 * live <= n <= 126 * live, (obj, lo, n, live)
+            assert n < 126 * live          # the bounds prune something on these weights
+    neg = -h
+    assert nv.scale_search_scored(W, neg, S, nv.WMSE, -8) == 126 * live
+    # the count accumulates
+    c = torch.full((1,), 5, dtype=torch.int64, device=DEV)
+    nv.nvfp4_scale_search_scored(W, 1, 152, 288, 288, 0, 16, h, 0, nv.WMSE, -8, S, c)
+    torch.cuda.synchronize()
+    assert int(c.item()) == 5 + nv.scale_search_scored(W, h, S, nv.WMSE, -8)
