@@ -78,6 +78,27 @@ __device__ __forceinline__ void load_h(const float* __restrict__ hm, bool valid,
     }
 }
 
+// The 16 h values of group g of a row, read by every lane (g must be a group of the row); zeros
+// when not needed.
+template <bool NEED_H>
+__device__ __forceinline__ void load_h_at(const float* __restrict__ hm, uint32_t g,
+                                          float (&h)[16]) {
+    if constexpr (NEED_H) {
+        const float4* hp = reinterpret_cast<const float4*>(hm + (int64_t)g * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 v = hp[i];
+            h[4 * i] = v.x;
+            h[4 * i + 1] = v.y;
+            h[4 * i + 2] = v.z;
+            h[4 * i + 3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 16; ++j) h[j] = 0.0f;
+    }
+}
+
 // One lane's group: its 16 weights and, when a rule needs them, its 16 h values.
 template <bool BF16, bool NEED_H>
 __device__ __forceinline__ void load_inputs(const uint8_t* __restrict__ Wm, int64_t ldw_bytes,
@@ -323,7 +344,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         for (int q = 0; q < U; ++q) a[q] = wraw[(wave0 + owner) * U + q];
         float w[16], h[16];
         unpack_group<BF16>(a, w);
-        load_h<WMSE>(hm, ovalid, og, h);
+        load_h_at<WMSE>(hm, og, h);      // idle lanes read group 0's h and use none of it
         float bl = __builtin_inff();
         int cl = 255;
         scan8<WMSE>(w, h, tab, first, bl, cl);

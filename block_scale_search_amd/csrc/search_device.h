@@ -205,7 +205,9 @@ __device__ __forceinline__ float bound_above(const float (&w)[16], const float (
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         const float a = fabsf(w[j]);
-        const float t = a < half ? fminf(a, half - a) : 0.0f;
+        // a < half: min(a, half - a), both non-negative; a >= half: half - a <= 0, so 0. The
+        // median of (a, half - a, 0) is exactly that, in one instruction.
+        const float t = __builtin_amdgcn_fmed3f(a, half - a, 0.0f);
         B = WMSE ? __builtin_fmaf(h[j] * t, t, B) : __builtin_fmaf(t, t, B);
     }
     return B;
@@ -274,6 +276,43 @@ __device__ __forceinline__ int centre_scan(const float (&w)[16], const float (&h
     return c0;
 }
 
+// Blocks needed in one direction from the centre: blocks k = 0 .. all - 1 start at code
+// first + 8k (UP) or end at code first - 8k (down), and block k, with every block beyond it, is
+// skipped when its bound B_k exceeds thr (and is finite). B_k is nondecreasing in k (the
+// effective scale grows, or shrinks, monotonically, and every step of the bound is monotone in
+// it), so a pruned block 1 leaves block 0's test to decide between 0 and 1 blocks, and a kept
+// block 1 means at least 2: the second test runs at block 0 or block 2 per lane, one pass for
+// the whole wave, and only lanes needing 3 blocks or more test further. (Where B_1 overflows
+// to +inf, blocks 0 and 1 are both kept: more blocks, never fewer, than the tests allow.)
+template <bool WMSE, bool UP>
+__device__ __forceinline__ int blocks_needed(const float (&w)[16], const float (&h)[16],
+                                             const float2* __restrict__ tab, int first, int all,
+                                             float thr) {
+    auto needed = [&](int k) {
+        const float e = tab[UP ? first + 8 * k : first - 8 * k].x;
+        const float B = UP ? bound_above<WMSE>(w, h, e) : bound_below<WMSE>(w, h, e);
+        return !(B > thr && B <= 0x1.fffffep127f);
+    };
+    int n = 0;
+    if (all > 0) {
+        const bool na = needed(min(1, all - 1));
+        const int kb = na ? 2 : 0;
+        bool nb = false;
+        if (all >= 2 && kb < all) nb = needed(kb);
+        if (all == 1) {
+            n = na ? 1 : 0;
+        } else if (!na) {
+            n = nb ? 1 : 0;
+        } else if (all == 2 || !nb) {
+            n = 2;
+        } else {
+            n = 3;
+            while (n < all && needed(n)) ++n;
+        }
+    }
+    return n;
+}
+
 // Phase 1, second half: the numbers of 8-code blocks needed above the centre block (n_up, from
 // code c0 + 16) and below it (n_dn, down from code c0 - 1), given the centre's best loss.
 template <bool WMSE>
@@ -304,16 +343,8 @@ __device__ __forceinline__ void pending_blocks(const float (&w)[16], const float
         return;
     }
     const float thr = __builtin_fmaf(best, 0x1p-14f, best);
-    while (n_up < all_up) {
-        const float B = bound_above<WMSE>(w, h, tab[up + 8 * n_up].x);
-        if (B > thr && B <= 0x1.fffffep127f) break;
-        ++n_up;
-    }
-    while (n_dn < all_dn) {
-        const float B = bound_below<WMSE>(w, h, tab[dn - 8 * n_dn].x);
-        if (B > thr && B <= 0x1.fffffep127f) break;
-        ++n_dn;
-    }
+    n_up = blocks_needed<WMSE, true>(w, h, tab, up, all_up, thr);
+    n_dn = blocks_needed<WMSE, false>(w, h, tab, dn, all_dn, thr);
 }
 
 // (loss, code) as one 64-bit key whose unsigned order is the lexicographic order of the scan:
