@@ -116,12 +116,25 @@ def paired_modes(cfg):
     return plain
 
 
+def nested_windows(modes) -> bool:
+    """Two windows the library scans as one (k_scale_search_nested): one of 16 codes holding the
+    other, which has 11 codes ending where the outer ends, or the same 16 codes."""
+    if len(modes) != 2 or any(m.exhaustive or m.proposal for m in modes):
+        return False
+    for o, i in (modes, modes[::-1]):
+        if n_candidates(o) == 16 and (i.lo - o.lo, n_candidates(i)) in ((5, 11), (0, 16)):
+            return True
+    return False
+
+
 def kernel_name(cfg, label: str) -> str:
     modes = label_modes(cfg, label)
     what = base_label(label)[len("search:"):]
     if any(m.exhaustive for m in modes):
         return f"k_scale_search_exhaustive {what}" + (" (one fused launch)" if len(modes) > 1
                                                       else "")
+    if nested_windows(modes):
+        return f"k_scale_search_nested {what}"
     return f"k_scale_search_pair {what}" if len(modes) > 1 else f"k_scale_search {what}"
 
 

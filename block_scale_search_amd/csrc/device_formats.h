@@ -55,6 +55,25 @@ __device__ __forceinline__ void e2m1_round8(const float (&x)[8], float pow2, flo
     q[4] = v2[0]; q[5] = v2[1]; q[6] = v3[0]; q[7] = v3[1];
 }
 
+// E2M1 codes of x[0..7] / pow2 (round to nearest even) in one dword, two per byte, x[2k] in
+// the low nibble of byte k: the down-conversion half of e2m1_round8.
+__device__ __forceinline__ uint32_t e2m1_codes8(const float (&x)[8], float pow2) {
+    uint32_t p = __float_as_uint(x[0]);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[0], x[1], pow2, 0);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[2], x[3], pow2, 1);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[4], x[5], pow2, 2);
+    p = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(p, x[6], x[7], pow2, 3);
+    return p;
+}
+
+// The levels of the two codes in byte SEL of p, as binary32 values.
+template <int SEL>
+__device__ __forceinline__ void e2m1_levels2(uint32_t p, float& q0, float& q1) {
+    const auto v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(p, 1.0f, SEL);
+    q0 = v[0];
+    q1 = v[1];
+}
+
 // Signed E2M1 codes of (x0, x1) written into byte `sel` of `word` (x0 -> low nibble).
 template <int SEL>
 __device__ __forceinline__ uint32_t e2m1_pack2(uint32_t word, float x0, float x1) {

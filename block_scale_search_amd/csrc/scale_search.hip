@@ -460,6 +460,53 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_pair(
     }
 }
 
+// Two windowed rules (bf16 W) where one window of 16 codes (outer, objective WO, offsets
+// loO .. loO + 15) contains the other (inner, objective WI, codes base + loO + OFFB ..
+// + NB - 1): where every lane's outer window is normal and unclipped, each 16-code block is
+// scanned once for both (scan_block_two: shared multiply, conversions and residuals). Other
+// waves run the two windows one after the other, as k_scale_search_pair does. Each rule's
+// outputs are those of k_scale_search.
+template <bool WO, bool WI, int OFFB, int NB>
+__global__ __launch_bounds__(kSearchThreads) __attribute__((amdgpu_waves_per_eu(7, 8))) void
+k_scale_search_nested(
+    const uint8_t* __restrict__ W, uint32_t out, uint32_t in, uint64_t gpr_magic,
+    uint32_t gpr_shift, int64_t ldw_bytes, int64_t stride_w_bytes, const float* __restrict__ hvec,
+    int64_t stride_h, const float* __restrict__ S_arr, int loO, RuleOut O, RuleOut I) {
+    __shared__ float2 tab[128];
+    __shared__ int flag;
+    const int64_t batch = blockIdx.y;
+    const uint32_t gpr = in >> 4;
+    const uint32_t G = out * gpr;
+    const uint32_t gi = blockIdx.x * kSearchThreads + threadIdx.x;
+    const bool valid = gi < G;
+    const uint32_t row = valid ? div_gpr(gi, gpr_magic, gpr_shift) : 0u;
+    const uint32_t g = valid ? gi - row * gpr : 0u;
+    float w[16], h[16];
+    load_inputs<true, WO || WI>(W + batch * stride_w_bytes, ldw_bytes, hvec + batch * stride_h,
+                                valid, row, g, w, h);
+    const float S = S_arr[batch];
+    const bool octave_ok = build_table(S, tab, &flag);
+    const int b = base_code(w, S);
+    const bool live = valid && b > 0;
+    const int64_t gidx = batch * (int64_t)G + gi;
+    const int loI = loO + OFFB;
+    float bestO = __builtin_inff(), bestI = __builtin_inff();
+    int cO = min(max(b + loO, 1), 126), cI = min(max(b + loI, 1), 126);
+    // idle lanes score the dummy codes 8 .. 23
+    const bool lane_fast = !live || (b + loO >= 8 && b + loO + 15 <= 126);
+    if (octave_ok && __all(lane_fast)) {
+        const int c0 = live ? b + loO : 8;
+        scan_block_two<WO, WI, OFFB, NB>(w, h, tab + c0, c0, bestO, cO, bestI, cI);
+    } else {
+        search_window<WO, 16>(w, h, tab, octave_ok, live, b + loO, 16, bestO, cO);
+        search_window<WI, NB>(w, h, tab, octave_ok, live, b + loI, NB, bestI, cI);
+    }
+    if (valid) {
+        emit_group(w, tab, live ? cO : 0, live ? bestO : 0.0f, live ? cO - b : 0, gidx, O);
+        emit_group(w, tab, live ? cI : 0, live ? bestI : 0.0f, live ? cI - b : 0, gidx, I);
+    }
+}
+
 }  // namespace
 
 namespace {
@@ -513,6 +560,40 @@ void launch_pair_t(const SearchArgs& a, const float* S, int loA, int loB, const 
     hipLaunchKernelGGL((k_scale_search_pair<WA, NA, WB, NB>), grid, dim3(kSearchThreads), 0,
                        stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes, a.stride_w_bytes,
                        a.h, a.stride_h, S, loA, loB, A, B);
+}
+
+template <bool WO, bool WI, int OFFB, int NB>
+void launch_nested_t(const SearchArgs& a, const float* S, const SearchRule& outer,
+                     const SearchRule& inner, dim3 grid, hipStream_t stream) {
+    hipLaunchKernelGGL((k_scale_search_nested<WO, WI, OFFB, NB>), grid, dim3(kSearchThreads), 0,
+                       stream, a.W, a.out, a.in, a.magic, a.shift, a.ldw_bytes, a.stride_w_bytes,
+                       a.h, a.stride_h, S, outer.lo, outer.out, inner.out);
+}
+
+// Two windowed rules whose one window of 16 codes holds the other, in one of the compiled
+// shapes: the inner window of 11 codes ending where the outer one ends (MSE [-3,7] inside
+// [-8,7]), or the same 16 codes. Returns false (nothing launched) for other pairs.
+bool launch_nested(const SearchArgs& a, const float* S, const SearchRule& r, const SearchRule& q,
+                   dim3 grid, hipStream_t stream) {
+    const int nr = r.hi - r.lo + 1, nq = q.hi - q.lo + 1;
+    const bool r_outer = nr == 16 && (nq != 16 || !r.wmse || q.wmse);
+    const SearchRule& outer = r_outer ? r : q;
+    const SearchRule& inner = r_outer ? q : r;
+    const int n_in = inner.hi - inner.lo + 1;
+    const int off = inner.lo - outer.lo;
+    if (outer.hi - outer.lo + 1 != 16) return false;
+#define NVFP4_NEST(OFF, N)                                                                     \
+    if (off == OFF && n_in == N) {                                                             \
+        if (outer.wmse && inner.wmse) launch_nested_t<true, true, OFF, N>(a, S, outer, inner, grid, stream);   \
+        else if (outer.wmse) launch_nested_t<true, false, OFF, N>(a, S, outer, inner, grid, stream);           \
+        else if (inner.wmse) launch_nested_t<false, true, OFF, N>(a, S, outer, inner, grid, stream);           \
+        else launch_nested_t<false, false, OFF, N>(a, S, outer, inner, grid, stream);                          \
+        return true;                                                                           \
+    }
+    NVFP4_NEST(5, 11)
+    NVFP4_NEST(0, 16)
+#undef NVFP4_NEST
+    return false;
 }
 
 template <bool WA, int NA>
@@ -574,6 +655,10 @@ hipError_t launch_scale_search_rules(const void* W, bool bf16, int64_t batch, in
         const SearchRule& r = rules[i];
         if (bf16 && i + 1 < n_rules && pairable(r) && pairable(rules[i + 1])) {
             const SearchRule& q = rules[i + 1];
+            if (launch_nested(a, S, r, q, grid, stream)) {
+                i += 2;
+                continue;
+            }
             const int na = r.hi - r.lo + 1;
             if (r.wmse) {
                 if (na == 16) launch_pair_b<true, 16>(a, S, r, q, grid, stream);

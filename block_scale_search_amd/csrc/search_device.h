@@ -87,6 +87,82 @@ __device__ __forceinline__ void loss_pair(const float (&w)[16], const float (&h)
     L_hi = quad_tree(Q);
 }
 
+// Losses of codes c (lo) and c + 8 (hi) under objective A and, where BLO / BHI, under objective
+// B as well: both objectives share the multiply, the conversions and the residuals, and differ
+// only in the weighting and the accumulation (each loss keeps the fixed tree order). With equal
+// objectives the B losses are the A losses.
+template <bool WA, bool WB, bool BLO, bool BHI, int QD, int HALF>
+__device__ __forceinline__ void two_quad(const float (&w)[16], const float (&h)[16], uint32_t pq,
+                                         uint32_t ps, float eff, float eff_hi, float& PA,
+                                         float& QA, float& PB, float& QB) {
+    constexpr bool OWN_B = WA != WB;
+    float q[4], s[4];
+    e2m1_levels2<2 * QD>(pq, q[0], q[1]);
+    e2m1_levels2<2 * QD + 1>(pq, q[2], q[3]);
+    e2m1_levels2<2 * QD>(ps, s[0], s[1]);
+    e2m1_levels2<2 * QD + 1>(ps, s[2], s[3]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int j = 8 * HALF + 4 * QD + i;
+        const float a = fabsf(w[j]);
+        const float d = __builtin_fmaf(-q[i], eff, a);
+        const float e = __builtin_fmaf(-s[i], eff_hi, a);
+        const float u = WA ? h[j] * d : d;
+        const float v = WA ? h[j] * e : e;
+        PA = i == 0 ? u * d : __builtin_fmaf(u, d, PA);
+        QA = i == 0 ? v * e : __builtin_fmaf(v, e, QA);
+        if constexpr (OWN_B && BLO) {
+            const float ub = WB ? h[j] * d : d;
+            PB = i == 0 ? ub * d : __builtin_fmaf(ub, d, PB);
+        }
+        if constexpr (OWN_B && BHI) {
+            const float vb = WB ? h[j] * e : e;
+            QB = i == 0 ? vb * e : __builtin_fmaf(vb, e, QB);
+        }
+    }
+}
+
+template <bool WA, bool WB, bool BLO, bool BHI, int HALF>
+__device__ __forceinline__ void two_half(const float (&w)[16], const float (&h)[16], float eff,
+                                         float r, float eff_hi, float& A_lo, float& A_hi,
+                                         float& B_lo, float& B_hi) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = fabsf(w[8 * HALF + i]) * r;
+    const uint32_t pq = e2m1_codes8(x, 1.0f), ps = e2m1_codes8(x, 2.0f);
+    float PA0, QA0, PB0, QB0, PA1, QA1, PB1, QB1;
+    two_quad<WA, WB, BLO, BHI, 0, HALF>(w, h, pq, ps, eff, eff_hi, PA0, QA0, PB0, QB0);
+    two_quad<WA, WB, BLO, BHI, 1, HALF>(w, h, pq, ps, eff, eff_hi, PA1, QA1, PB1, QB1);
+    // the half's two quads: P_0 + P_1 (left) or P_2 + P_3 (right) of the loss tree
+    A_lo = PA0 + PA1;
+    A_hi = QA0 + QA1;
+    if constexpr (WA != WB && BLO) B_lo = PB0 + PB1;
+    if constexpr (WA != WB && BHI) B_hi = QB0 + QB1;
+}
+
+// Losses of codes c (lo) and c + 8 (hi) under objective A and, where BLO / BHI, under objective
+// B as well: both objectives share the multiply, the conversions and the residuals, and differ
+// only in the weighting and the accumulation. Each loss is the fixed tree
+// (P_0 + P_1) + (P_2 + P_3), its halves summed as soon as they are complete. With equal
+// objectives the B losses are the A losses.
+template <bool WA, bool WB, bool BLO, bool BHI>
+__device__ __forceinline__ void loss_pair_two(const float (&w)[16], const float (&h)[16],
+                                              float eff, float r, float eff_hi, float& A_lo,
+                                              float& A_hi, float& B_lo, float& B_hi) {
+    float la_lo, la_hi, lb_lo = 0.0f, lb_hi = 0.0f, ra_lo, ra_hi, rb_lo = 0.0f, rb_hi = 0.0f;
+    two_half<WA, WB, BLO, BHI, 0>(w, h, eff, r, eff_hi, la_lo, la_hi, lb_lo, lb_hi);
+    two_half<WA, WB, BLO, BHI, 1>(w, h, eff, r, eff_hi, ra_lo, ra_hi, rb_lo, rb_hi);
+    A_lo = la_lo + ra_lo;
+    A_hi = la_hi + ra_hi;
+    if constexpr (WA != WB) {
+        B_lo = lb_lo + rb_lo;
+        B_hi = lb_hi + rb_hi;
+    } else {
+        B_lo = A_lo;
+        B_hi = A_hi;
+    }
+}
+
 // Sequence point between candidates: an empty asm that reads and rewrites v, so everything that
 // produced v is done before it and everything that uses v comes after it. Without it the compiler
 // interleaves the arithmetic of several candidates, which raises the register count and lowers
@@ -134,6 +210,61 @@ __device__ __forceinline__ void scan_block(const float (&w)[16], const float (&h
     }
     keep_min(bl, c0 + pl, best, best_c);
     keep_min(bh, c0 + ph, best, best_c);
+}
+
+// Running minima of a 16-code block scanned for two windows at once: the outer window is the
+// block c0 .. c0 + 15 under objective WA, the inner one its codes c0 + OFFB .. c0 + OFFB + NB - 1
+// under objective WB. Each keeps the block's split into low codes (p < 8) and high codes
+// (p >= 8), both ascending, as scan_block does.
+struct TwoMins {
+    float blA, bhA, blB, bhB;
+    int plA, phA, plB, phB;
+};
+
+template <bool WA, bool WB, int OFFB, int NB, int P>
+__device__ __forceinline__ void two_step(const float (&w)[16], const float (&h)[16],
+                                         const float2* __restrict__ t0, TwoMins& m) {
+    constexpr bool BLO = P >= OFFB && P < OFFB + NB;
+    constexpr bool BHI = P + 8 >= OFFB && P + 8 < OFFB + NB;
+    float2 er = t0[P];
+    order_point(er.x);
+    order_point(er.y);
+    float Alo, Ahi, Blo, Bhi;
+    loss_pair_two<WA, WB, BLO, BHI>(w, h, er.x, er.y, t0[P + 8].x, Alo, Ahi, Blo, Bhi);
+    if (Alo < m.blA) { m.blA = Alo; m.plA = P; }
+    if (Ahi < m.bhA) { m.bhA = Ahi; m.phA = P + 8; }
+    if constexpr (BLO) {
+        if (Blo < m.blB) { m.blB = Blo; m.plB = P; }
+    }
+    if constexpr (BHI) {
+        if (Bhi < m.bhB) { m.bhB = Bhi; m.phB = P + 8; }
+    }
+    order_point(m.blA);
+    order_point(m.bhA);
+    order_point(m.blB);
+    order_point(m.bhB);
+}
+
+template <bool WA, bool WB, int OFFB, int NB>
+__device__ __forceinline__ void scan_block_two(const float (&w)[16], const float (&h)[16],
+                                               const float2* __restrict__ t0, int c0,
+                                               float& bestA, int& best_cA, float& bestB,
+                                               int& best_cB) {
+    static_assert(OFFB >= 0 && NB >= 1 && OFFB + NB <= 16, "inner window inside the block");
+    TwoMins m{__builtin_inff(), __builtin_inff(), __builtin_inff(), __builtin_inff(),
+              0, 8, 0, 8};
+    two_step<WA, WB, OFFB, NB, 0>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 1>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 2>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 3>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 4>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 5>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 6>(w, h, t0, m);
+    two_step<WA, WB, OFFB, NB, 7>(w, h, t0, m);
+    keep_min(m.blA, c0 + m.plA, bestA, best_cA);
+    keep_min(m.bhA, c0 + m.phA, bestA, best_cA);
+    keep_min(m.blB, c0 + m.plB, bestB, best_cB);
+    keep_min(m.bhB, c0 + m.phB, bestB, best_cB);
 }
 
 // Windowed search of one lane: codes first .. first + n - 1 (the window base + lo .. base + hi).

@@ -237,7 +237,10 @@ nvfp4_status nvfp4_scale_search(const void* W, int w_dtype, int64_t batch, int64
  * exhaustive and output pointers, and the call's other arguments. Rules are taken in order,
  * two at a time where they fit one launch:
  *   - two consecutive windowed rules of 11 or 16 codes on bf16 W run as one launch that reads
- *     each group once and shares its table and base code between them;
+ *     each group once and shares its table and base code between them; where one window has
+ *     16 codes and holds the other (11 codes ending where it ends, as MSE [-3, 7] inside
+ *     [-8, 7], or the same 16 codes), each code is converted once for both rules and only the
+ *     weighting and the sum of squares are done per rule;
  *   - else a windowed rule of 16 codes and an exhaustive rule of the same objective, next to
  *     each other in either order (bf16 or f32 W), run as one launch: the exhaustive search's
  *     first block of 16 codes is placed on the window, so the window's losses are the ones the

@@ -61,6 +61,8 @@ def test_paired_launch_counts_both_rules():
     cfg = C["attn8b"]
     assert [m.label for m in bench.paired_modes(cfg)] == ["MSE [-3,7]", "WMSE [-8,7]"]
     label = bench.pair_label(bench.paired_modes(cfg))
+    # MSE [-3,7] lies inside WMSE [-8,7]: one scan of the 16 codes serves both
+    assert bench.kernel_name(cfg, label).startswith("k_scale_search_nested")
     flops, ops = bench.search_work(cfg, label)
     n_w = 4096 * 4096
     assert flops == n_w * (11 * 5 + 16 * 6)

@@ -44,11 +44,14 @@ def _check(nv, W, h, S, rules, what):
         assert_same(g, o, f"{what} rule ({obj}, {lo}, {hi}, {exh})")
 
 
-PAIRS = [[(0, -3, 7, False), (1, -8, 7, False)],      # the 8B attention modes
+PAIRS = [[(0, -3, 7, False), (1, -8, 7, False)],      # the 8B attention modes (nested windows)
          [(1, -9, 6, False), (0, -3, 7, False)],
          [(1, -8, 7, False), (1, -9, 6, False)],
          [(0, -3, 7, False), (0, -5, 5, False)],
-         [(1, -3, 7, False), (0, -8, 7, False)]]
+         [(1, -3, 7, False), (0, -8, 7, False)],      # nested, MSE outside
+         [(1, -9, 6, False), (0, -4, 6, False)],      # nested, the 11 codes ending at +6
+         [(0, -8, 7, False), (1, -8, 7, False)],      # the same 16 codes, two objectives
+         [(1, -8, 7, False), (1, -3, 7, False)]]      # nested, one objective
 
 
 @pytest.mark.parametrize("rules", PAIRS, ids=lambda r: "+".join(f"{o}[{lo},{hi}]" for o, lo, hi, _ in r))
@@ -182,3 +185,16 @@ def test_scored_count(nv):
     nv.nvfp4_scale_search_scored(W, 1, 152, 288, 288, 0, 16, h, 0, nv.WMSE, -8, S, c)
     torch.cuda.synchronize()
     assert int(c.item()) == 5 + nv.scale_search_scored(W, h, S, nv.WMSE, -8)
+
+
+@pytest.mark.parametrize("rules", [[(0, -3, 7, False), (1, -8, 7, False)],
+                                   [(1, -8, 7, False), (0, -8, 7, False)]],
+                         ids=["mse[-3,7]+wmse[-8,7]", "wmse[-8,7]+mse[-8,7]"])
+def test_nested_windows_over_the_code_range(nv, rules):
+    """Nested windows in one launch where waves mix unclipped, clipped and subnormal windows
+    (those waves take the one-window-at-a-time path), against the separate calls and the
+    oracle."""
+    W, h = _wide_range(152, 288, torch.bfloat16, seed=63)
+    W[0] = 0.0
+    S = nv.global_scale(W, nv.GS_AMAX_448)
+    _check(nv, W, h, S, rules, "nested wide range")
