@@ -154,12 +154,21 @@ __device__ __forceinline__ void hess_partial_body(const uint8_t* __restrict__ X,
     const bool active = col < in;
     const uint8_t* base = X + col * (BF16 ? 2 : 4);
     const int64_t blocks = (row1 - row0 + V - 1) / V;  // V-row blocks
-    const int64_t full = (row1 - row0) / V;             // complete ones
 
     double acc[C];
 #pragma unroll
     for (int i = 0; i < C; ++i) acc[i] = 0.0;
-    auto add_squares = [&](const uint4 (&v)[kLoads]) {
+    for (int64_t j0 = g; j0 < blocks; j0 += count * kLoads) {
+        uint4 v[kLoads];
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            const int64_t j = j0 + (int64_t)k * count;
+            const int64_t r = row0 + j * V + wave;
+            if (active && j < blocks && r < row1)
+                v[k] = load_stream(base + r * ldx_bytes);
+            else
+                v[k] = make_uint4(0u, 0u, 0u, 0u);
+        }
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) {
             const uint32_t d[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
@@ -178,33 +187,6 @@ __device__ __forceinline__ void hess_partial_body(const uint8_t* __restrict__ X,
                 }
             }
         }
-    };
-    // Block sequence j = g, g + count, g + 2 count, ..., kLoads of them per step. While all
-    // kLoads blocks of a step are complete every row exists, so the loads need no test (a lane
-    // past the last column reads column 0 of the same rows and its sums are never stored); the
-    // remaining steps test each row and add zeros for the missing ones. Both visit the blocks
-    // in the same order, so the sums do not depend on where the split falls.
-    const uint8_t* safe = active ? base : X;
-    int64_t j0 = g;
-    for (; j0 + (int64_t)(kLoads - 1) * count < full; j0 += count * kLoads) {
-        uint4 v[kLoads];
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k)
-            v[k] = load_stream(safe + (row0 + (j0 + (int64_t)k * count) * V + wave) * ldx_bytes);
-        add_squares(v);
-    }
-    for (; j0 < blocks; j0 += count * kLoads) {
-        uint4 v[kLoads];
-#pragma unroll
-        for (int k = 0; k < kLoads; ++k) {
-            const int64_t j = j0 + (int64_t)k * count;
-            const int64_t r = row0 + j * V + wave;
-            if (active && j < blocks && r < row1)
-                v[k] = load_stream(base + r * ldx_bytes);
-            else
-                v[k] = make_uint4(0u, 0u, 0u, 0u);
-        }
-        add_squares(v);
     }
 #pragma unroll
     for (int i = 0; i < C; ++i) red[wave][lane * C + i] = acc[i];
@@ -219,7 +201,7 @@ __device__ __forceinline__ void hess_partial_body(const uint8_t* __restrict__ X,
 }
 
 template <bool BF16, int V>
-__global__ __launch_bounds__(64 * V) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_hess_partial(const uint8_t* __restrict__ X,
+__global__ __launch_bounds__(64 * V) void k_hess_partial(const uint8_t* __restrict__ X,
                                                          int64_t in, int64_t ldx_bytes,
                                                          GroupMap map, int64_t n_strips,
                                                          double* __restrict__ partial, int add) {
@@ -285,7 +267,7 @@ __global__ __launch_bounds__(kFinThreads) void k_hess_finalize(const double* __r
 // [blk_prefix[c], blk_prefix[c + 1]) run the single-segment partial pass over chunk c into the
 // slots [slot_prefix[c], slot_prefix[c + 1]); one finalize then sums every slot.
 template <bool BF16, int V>
-__global__ __launch_bounds__(64 * V) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_hess_partial_chunks(ChunkTable ct, int64_t in,
+__global__ __launch_bounds__(64 * V) void k_hess_partial_chunks(ChunkTable ct, int64_t in,
                                                                 int64_t ldx_bytes,
                                                                 int64_t n_strips,
                                                                 double* __restrict__ partial) {
@@ -302,7 +284,7 @@ __global__ __launch_bounds__(64 * V) __attribute__((amdgpu_waves_per_eu(8, 8))) 
 // Layer statistics, pass 1: the first n_hess workgroups are the h partial pass over X, the rest
 // the amax partial pass over W (both streaming, one launch).
 template <bool XBF16, int V, bool WBF16>
-__global__ __launch_bounds__(64 * V) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_stats_partial(
+__global__ __launch_bounds__(64 * V) void k_stats_partial(
     const uint8_t* __restrict__ X, int64_t in, int64_t ldx_bytes, GroupMap map, int64_t n_strips,
     double* __restrict__ partial, int64_t n_hess, const uint8_t* __restrict__ W, int64_t out,
     AmaxPlan ap, int64_t ldw_bytes, uint32_t* __restrict__ amax_partial) {
