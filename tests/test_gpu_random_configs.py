@@ -63,3 +63,47 @@ def test_random_configuration(nv, i):
     o = oracle_search(W, h if objective == "wmse" else None, S_o if len(S_o) > 1 else S_o[0],
                       objective, lo, hi, exhaustive)
     assert_same(g, o, f"case {i}: {tuple(W.shape)} {W.dtype} {objective} [{lo},{hi}] exh={exhaustive}")
+
+
+N_RULE_CASES = 16
+
+
+def _rule_pair(i: int):
+    """Two rules that one launch serves: a 16-code window with the exhaustive mode of its
+    objective (bf16 or f32), or nested windows on bf16 (11 codes ending where the 16 end, or the
+    same 16 codes under both objectives), in either order."""
+    rng = np.random.default_rng(9500 + i)
+    obj = [int(rng.integers(0, 2)), int(rng.integers(0, 2))]
+    lo = -int(rng.integers(0, 16))
+    if i % 2 == 0:
+        rules = [(obj[0], lo, lo + 15, False), (obj[0], 0, 0, True)]
+    elif i % 4 == 1:
+        lo = min(lo, -5)                # the inner window [lo + 5, lo + 15] must hold offset 0
+        rules = [(obj[0], lo, lo + 15, False), (obj[1], lo + 5, lo + 15, False)]
+    else:
+        rules = [(0, lo, lo + 15, False), (1, lo, lo + 15, False)]
+    if rng.random() < 0.5:
+        rules = rules[::-1]
+    return rules
+
+
+@pytest.mark.parametrize("i", range(N_RULE_CASES))
+def test_random_rule_pairs(nv, i):
+    W, h, _, _, _, _, rule = _case(100 + i)
+    rules = _rule_pair(i)
+    if not any(r[3] for r in rules) and W.dtype != torch.bfloat16:
+        W = W.to(torch.bfloat16)
+    S = nv.global_scale(W, nv.GS_AMAX_448 if rule == 0 else nv.GS_AMAX_256)
+    Sn = S.cpu().numpy().reshape(-1)
+    ht = torch.from_numpy(h).to(DEV)
+    got = nv.scale_search_rules(W, ht, S, rules)
+    torch.cuda.synchronize()
+    for (obj, lo, hi, exh), r in zip(rules, got):
+        g = {k: v.cpu().numpy() for k, v in r.items()}
+        if W.dim() == 2:
+            g = {k: v[None] for k, v in g.items()}
+        wm = obj == nv.WMSE
+        o = oracle_search(W, h if wm else None, Sn if W.dim() == 3 else float(Sn[0]),
+                          "wmse" if wm else "mse", lo, hi, exh)
+        assert_same(g, o, f"rule case {i}: {tuple(W.shape)} {W.dtype} rules {rules}, "
+                          f"rule ({obj}, {lo}, {hi}, {exh})")
