@@ -865,7 +865,7 @@ def main():
         "achieved": round(achieved, 2), "peak": VALU_PUBLISHED_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / VALU_PUBLISHED_TFLOPS, 4),
         "traffic": read_traffic(args.workload, dom),
-        "alg_flops_per_launch": g["flops"] // g["launches"],
+        "alg_flops_per_launch": int(round(g["flops"] / g["launches"])),
         "avg_launch_us": round(us_launch, 3), "launches_per_step": g["launches"],
         "flops_per_element_candidate": FLOPS_PER_ELEM_CAND,
         "flops_counted": ("element-candidates the exhaustive search scores (its first block of "
