@@ -1,7 +1,8 @@
 """GPU parity of nvfp4_scale_search_rules: several rules in one call give, rule by rule, the
 bytes of separate nvfp4_scale_search calls and of the oracle (paired launches for windows of
-11 and 16 codes on bf16 W, one fused launch for a 16-code window next to an exhaustive rule of
-the same objective, single launches for the rest)."""
+11 and 16 codes on bf16 W, scanned once where one 16-code window holds the other; one fused
+launch for a 16-code window next to an exhaustive rule of the same objective; single launches
+for the rest)."""
 import numpy as np
 import pytest
 import torch
