@@ -869,7 +869,7 @@ def main():
         "avg_launch_us": round(us_launch, 3), "launches_per_step": g["launches"],
         "flops_per_element_candidate": FLOPS_PER_ELEM_CAND,
         "flops_counted": ("element-candidates the exhaustive search scores (its first block of "
-                          "16 codes, which is the fused window, plus every block of 8 that its "
+                          "16 codes, which is the fused window, plus every block of 4 that its "
                           "exact lower bounds keep; nvfp4_scale_search_scored on the same "
                           "inputs), x flops per element-candidate" if pruned else
                           "every candidate of the window for every weight, x flops per "

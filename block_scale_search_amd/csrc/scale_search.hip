@@ -226,8 +226,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search(
 }
 
 // Exhaustive mode (every code 1..126): the three phases of search_device.h's exhaustive search.
-// Phase 1 per lane (centre block, pending block counts), phase 2 the wave's pending 8-code
-// blocks dealt over its lanes, phase 3 each lane's result from its LDS slot, then the output.
+// Phase 1 per lane (centre block, pending block counts), phase 2 the workgroup's pending blocks
+// dealt over its lanes, phase 3 each lane's result from its LDS slot, then the output.
 // Each lane keeps its group's raw bytes in LDS from phase 1 on, and h is read again from memory
 // (a few KB per matrix, always cached), so that phase 2 (another lane's group) and the output
 // need no registers held through the kernel (the register count, and the waves per SIMD, stay
@@ -245,7 +245,9 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     int64_t stride_h, const float* __restrict__ S_arr, RuleOut o, int wlo, RuleOut ow) {
     __shared__ float2 tab[128];
     __shared__ int flag;
-    __shared__ int first_item[kSearchThreads];             // per wave: exclusive prefix of counts
+    __shared__ int first_item[kSearchThreads];             // exclusive prefix of the counts
+    __shared__ int owner_info[kSearchThreads];             // per lane: c0 | n_up << 8
+    __shared__ int wave_items[kSearchThreads / 64];        // per wave: its lanes' items
     __shared__ unsigned long long slot[kSearchThreads];    // per lane: min (loss, code) key
     constexpr int U = kGroupUnits<BF16>;
     __shared__ uint4 wraw[kSearchThreads * U];              // per lane: its group's raw bytes
@@ -309,7 +311,8 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         slot[threadIdx.x] = loss_key(best, best_c);
     }
 
-    // phase 2: exclusive prefix of the lanes' block counts, then rounds of one block per lane
+    // phase 2: the workgroup's pending blocks in item order (lane by lane), 64 items per wave
+    // and round, the waves taking rounds in turn
     const int n = n_up + n_dn;
     int incl = n;
 #pragma unroll
@@ -317,38 +320,49 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         const int v = __shfl_up(incl, d, 64);
         if (lane >= d) incl += v;
     }
-    const int total = __shfl(incl, 63, 64);
-    first_item[threadIdx.x] = incl - n;
+    if (lane == 63) wave_items[threadIdx.x >> 6] = incl;
+    owner_info[threadIdx.x] = c0 | (n_up << 8);
     __syncthreads();
-    for (int t0 = 0; t0 < total; t0 += 64) {
+    int before = 0, total = 0;
+#pragma unroll
+    for (int q = 0; q < kSearchThreads / 64; ++q) {
+        const int v = wave_items[q];
+        before += q < (int)(threadIdx.x >> 6) ? v : 0;
+        total += v;
+    }
+    first_item[threadIdx.x] = before + incl - n;
+    __syncthreads();
+    for (int t0 = (int)wave0; t0 < total; t0 += kSearchThreads) {
         const int t = t0 + lane;
         const bool has = t < total;
         // owner: the last lane whose first item is <= t (lanes without items share the next
         // lane's first item and are passed over)
         int j = 0;
 #pragma unroll
-        for (int step = 32; step >= 1; step >>= 1)
-            if (first_item[wave0 + j + step] <= t) j += step;
-        const int owner = has ? j : lane;
-        const int k = t - first_item[wave0 + owner];
-        const int o_up = __shfl(n_up, owner, 64);
-        const int o_c0 = __shfl(c0, owner, 64);
+        for (int step = kSearchThreads / 2; step >= 1; step >>= 1)
+            if (first_item[j + step] <= t) j += step;
+        const int owner = has ? j : (int)threadIdx.x;
+        const int k = t - first_item[owner];
+        const int info = owner_info[owner];
+        const int o_c0 = info & 255, o_up = info >> 8;
         // block k of the owner: upward from o_c0 + 16, then downward from o_c0 - 1
-        const int first = !has ? 8 : (k < o_up ? o_c0 + 16 + 8 * k : o_c0 - 8 * (k - o_up) - 8);
-        const uint32_t ogi = blockIdx.x * kSearchThreads + wave0 + owner;
+        const int first = !has ? 8
+                               : (k < o_up ? o_c0 + 16 + kBlockCodes * k
+                                           : o_c0 - kBlockCodes * (k - o_up + 1));
+        const uint32_t ogi = blockIdx.x * kSearchThreads + owner;
         const bool ovalid = has && ogi < G;
         const uint32_t orow = ovalid ? div_gpr(ogi, gpr_magic, gpr_shift) : 0u;
         const uint32_t og = ovalid ? ogi - orow * gpr : 0u;
         uint4 a[U];
 #pragma unroll
-        for (int q = 0; q < U; ++q) a[q] = wraw[(wave0 + owner) * U + q];
+        for (int q = 0; q < U; ++q) a[q] = wraw[owner * U + q];
         float w[16], h[16];
         unpack_group<BF16>(a, w);
         load_h_at<WMSE>(hm, og, h);      // idle lanes read group 0's h and use none of it
         float bl = __builtin_inff();
         int cl = 255;
-        scan8<WMSE>(w, h, tab, first, bl, cl);
-        if (has) atomicMin(&slot[wave0 + owner], (unsigned long long)loss_key(bl, cl));
+        scan_codes<WMSE, kBlockCodes>(w, h, tab, first, bl, cl);
+        if (has) atomicMin(&slot[owner], (unsigned long long)loss_key(bl, cl));
     }
     __syncthreads();
 
@@ -404,7 +418,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_exhaustive_scored(
         const int c0 = centre_scan<WMSE>(w, h, tab, octave_ok, live, b, clo, best, best_c);
         pending_blocks<WMSE>(w, h, tab, live, c0, best, n_up, n_dn);
         const int up = c0 + 16, dn = c0 - 1;
-        if (live) n = 16 + (min(up + 8 * n_up, 127) - up) + min(8 * n_dn, dn);
+        if (live) n = 16 + (min(up + kBlockCodes * n_up, 127) - up) + min(kBlockCodes * n_dn, dn);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) n += __shfl_xor(n, d, 64);

@@ -344,13 +344,13 @@ __device__ __forceinline__ float bound_above(const float (&w)[16], const float (
     return B;
 }
 
-// Eight codes c0 .. c0 + 7 of one lane, each on its own; codes outside 1..126 are skipped.
-template <bool WMSE>
-__device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16],
-                                      const float2* __restrict__ tab, int c0, float& best,
-                                      int& best_c) {
+// N codes c0 .. c0 + N - 1 of one lane, each on its own; codes outside 1..126 are skipped.
+template <bool WMSE, int N>
+__device__ __forceinline__ void scan_codes(const float (&w)[16], const float (&h)[16],
+                                           const float2* __restrict__ tab, int c0, float& best,
+                                           int& best_c) {
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
+    for (int p = 0; p < N; ++p) {
         const int c = c0 + p;
         const bool in = c >= 1 && c <= 126;
         float2 er = tab[in ? c : 1];
@@ -362,10 +362,13 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
     }
 }
 
+// Codes per pending block of the exhaustive search (beyond the 16-code centre).
+constexpr int kBlockCodes = 4;
+
 // Exhaustive search over all 126 codes, with pruning that provably skips only losers, in three
-// phases per wave.
+// phases per workgroup.
 //  1. Each lane scores the 16 codes around its own base code (octave pairs when the table
-//     allows) and counts the blocks of 8 codes it still needs above and below them: a block,
+//     allows) and counts the blocks of kBlockCodes codes it still needs above and below them: a block,
 //     and every block beyond it, is skipped when a lower bound on the loss at the block's first
 //     code exceeds the lane's best loss by a relative margin of 2^-14. The margin covers the
 //     rounding of the binary32 loss tree and of the bound itself (each at most about 20
@@ -373,10 +376,11 @@ __device__ __forceinline__ void scan8(const float (&w)[16], const float (&h)[16]
 //     error analysis holds: non-negative finite h, a best loss of at least 2^-100 and
 //     amax (1 + max h) <= 2^100 best, so that underflowing products (absolute error 2^-150
 //     each) stay far below the margin; elsewhere the lane needs every block.
-//  2. The wave's pending blocks are dealt over its 64 lanes (a prefix of the per-lane counts
-//     in LDS tells each item's owner), so that the wave runs ceil(total / 64) rounds of 8 codes
-//     instead of as many as its busiest lane needs. A lane scoring another lane's block reloads
-//     that group's weights and h (recently read, so from the caches). Each block's lowest
+//  2. The workgroup's pending blocks are dealt over its lanes, 64 items per wave and round (a
+//     prefix of the per-lane counts in LDS tells each item's owner), so that the workgroup runs
+//     ceil(total / 64) wave-rounds of kBlockCodes codes instead of as many rounds as its busiest
+//     lane needs in every wave. A lane scoring another lane's block reloads that group's
+//     weights and h (recently read, so from the caches). Each block's lowest
 //     (loss, code) is merged into its owner's slot with an LDS 64-bit minimum on a key whose
 //     unsigned order is the (loss, code) order (loss_key below), so the merged result does not
 //     depend on the order of the merges.
@@ -401,14 +405,14 @@ __device__ __forceinline__ int centre_scan(const float (&w)[16], const float (&h
     if (octave_ok) {
         scan_block<WMSE, 16>(w, h, tab + c0, c0, 16, best, best_c);
     } else {
-        scan8<WMSE>(w, h, tab, c0, best, best_c);
-        scan8<WMSE>(w, h, tab, c0 + 8, best, best_c);
+        scan_codes<WMSE, 16>(w, h, tab, c0, best, best_c);
     }
     return c0;
 }
 
 // Blocks needed in one direction from the centre: blocks k = 0 .. all - 1 start at code
-// first + 8k (UP) or end at code first - 8k (down), and block k, with every block beyond it, is
+// first + kBlockCodes k (UP) or end at code first - kBlockCodes k (down), and block k, with
+// every block beyond it, is
 // skipped when its bound B_k exceeds thr (and is finite). B_k is nondecreasing in k (the
 // effective scale grows, or shrinks, monotonically, and every step of the bound is monotone in
 // it), so a pruned block 1 leaves block 0's test to decide between 0 and 1 blocks, and a kept
@@ -420,7 +424,7 @@ __device__ __forceinline__ int blocks_needed(const float (&w)[16], const float (
                                              const float2* __restrict__ tab, int first, int all,
                                              float thr) {
     auto needed = [&](int k) {
-        const float e = tab[UP ? first + 8 * k : first - 8 * k].x;
+        const float e = tab[UP ? first + kBlockCodes * k : first - kBlockCodes * k].x;
         const float B = UP ? bound_above<WMSE>(w, h, e) : bound_below<WMSE>(w, h, e);
         return !(B > thr && B <= 0x1.fffffep127f);
     };
@@ -444,7 +448,7 @@ __device__ __forceinline__ int blocks_needed(const float (&w)[16], const float (
     return n;
 }
 
-// Phase 1, second half: the numbers of 8-code blocks needed above the centre block (n_up, from
+// Phase 1, second half: the numbers of kBlockCodes-code blocks needed above the centre block (n_up, from
 // code c0 + 16) and below it (n_dn, down from code c0 - 1), given the centre's best loss.
 template <bool WMSE>
 __device__ __forceinline__ void pending_blocks(const float (&w)[16], const float (&h)[16],
@@ -465,8 +469,8 @@ __device__ __forceinline__ void pending_blocks(const float (&w)[16], const float
     }
     const float scale_ref = amax * (1.0f + hmax);
     const int up = c0 + 16, dn = c0 - 1;
-    const int all_up = up <= 126 ? (126 - up) / 8 + 1 : 0;
-    const int all_dn = dn >= 1 ? (dn - 1) / 8 + 1 : 0;
+    const int all_up = up <= 126 ? (126 - up) / kBlockCodes + 1 : 0;
+    const int all_dn = dn >= 1 ? (dn - 1) / kBlockCodes + 1 : 0;
     const bool can_prune = h_ok && best >= 0x1p-100f && scale_ref <= best * 0x1p100f;
     if (!can_prune) {
         n_up = all_up;

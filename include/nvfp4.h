@@ -277,7 +277,7 @@ nvfp4_status nvfp4_scale_search_rules(const void* W, int w_dtype, int64_t batch,
  * depend on the data). Adds to *count the number of (group, code) candidates that the
  * exhaustive search over these inputs scores: for every group with a nonzero base code, the 16
  * codes of its first block (codes clamp(base + centre_lo, 8, 111) .. + 15) and the codes 1..126
- * of every further block of 8 that its bounds do not rule out. It runs the search's own first
+ * of every further block of 4 that its bounds do not rule out. It runs the search's own first
  * phase, so the count is exact for the same W, h and S.
  *
  * centre_lo  -8 for nvfp4_scale_search's exhaustive mode; for nvfp4_scale_search_rules' fused
