@@ -247,6 +247,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
     __shared__ int flag;
     __shared__ int first_item[kSearchThreads];             // exclusive prefix of the counts
     __shared__ int owner_info[kSearchThreads];             // per lane: c0 | n_up << 8
+    __shared__ uint32_t owner_g[kSearchThreads];           // per lane: its group's column group
     __shared__ int wave_items[kSearchThreads / 64];        // per wave: its lanes' items
     __shared__ unsigned long long slot[kSearchThreads];    // per lane: min (loss, code) key
     constexpr int U = kGroupUnits<BF16>;
@@ -277,6 +278,7 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         load_h<WMSE>(hm, valid, g, h);
 #pragma unroll
         for (int k = 0; k < U; ++k) wraw[threadIdx.x * U + k] = a[k];
+        owner_g[threadIdx.x] = g;
         unpack_group<BF16>(a, w);
         const bool octave_ok = build_table(S, tab, &flag);
         b = base_code(w, S);
@@ -349,18 +351,16 @@ __global__ __launch_bounds__(kSearchThreads) void k_scale_search_exhaustive(
         const int first = !has ? 8
                                : (k < o_up ? o_c0 + 16 + kBlockCodes * k
                                            : o_c0 - kBlockCodes * (k - o_up + 1));
-        const uint32_t ogi = blockIdx.x * kSearchThreads + owner;
-        const bool ovalid = has && ogi < G;
-        const uint32_t orow = ovalid ? div_gpr(ogi, gpr_magic, gpr_shift) : 0u;
-        const uint32_t og = ovalid ? ogi - orow * gpr : 0u;
+        const uint32_t og = owner_g[owner];   // 0 for lanes past the last group
         uint4 a[U];
 #pragma unroll
         for (int q = 0; q < U; ++q) a[q] = wraw[owner * U + q];
         float w[16], h[16];
         unpack_group<BF16>(a, w);
-        load_h_at<WMSE>(hm, og, h);      // idle lanes read group 0's h and use none of it
+        load_h_at<WMSE>(hm, og, h);      // idle lanes read their own group's h and use none of it
+        // every block holds at least one code in 1..126, the first of them max(first, 1)
         float bl = __builtin_inff();
-        int cl = 255;
+        int cl = max(first, 1);
         scan_codes<WMSE, kBlockCodes>(w, h, tab, first, bl, cl);
         if (has) atomicMin(&slot[owner], (unsigned long long)loss_key(bl, cl));
     }

@@ -344,7 +344,10 @@ __device__ __forceinline__ float bound_above(const float (&w)[16], const float (
     return B;
 }
 
-// N codes c0 .. c0 + N - 1 of one lane, each on its own; codes outside 1..126 are skipped.
+// N codes c0 .. c0 + N - 1 of one lane, each on its own and in ascending order; codes outside
+// 1..126 are skipped. The caller starts the running minimum at (+inf, the first code in range),
+// so a strictly smaller loss replaces it and the result is the scan's first minimum, as on
+// (loss, code) lexicographically.
 template <bool WMSE, int N>
 __device__ __forceinline__ void scan_codes(const float (&w)[16], const float (&h)[16],
                                            const float2* __restrict__ tab, int c0, float& best,
@@ -357,7 +360,7 @@ __device__ __forceinline__ void scan_codes(const float (&w)[16], const float (&h
         order_point(er.x);
         order_point(er.y);
         const float L = loss_one<WMSE>(w, h, er.x, er.y);
-        if (in) keep_min_lex(L, c, best, best_c);
+        keep_min(in ? L : __builtin_inff(), c, best, best_c);
         order_point(best);
     }
 }
@@ -373,7 +376,8 @@ constexpr int kBlockCodes = 4;
 //     code exceeds the lane's best loss by a relative margin of 2^-14. The margin covers the
 //     rounding of the binary32 loss tree and of the bound itself (each at most about 20
 //     roundings of 2^-24 on sums of non-negative terms). The test is used only where that
-//     error analysis holds: non-negative finite h, a best loss of at least 2^-100 and
+//     error analysis holds: every h_j without sign bit and at most 2^100, a best loss of at
+//     least 2^-100 and
 //     amax (1 + max h) <= 2^100 best, so that underflowing products (absolute error 2^-150
 //     each) stay far below the margin; elsewhere the lane needs every block.
 //  2. The workgroup's pending blocks are dealt over its lanes, 64 items per wave and round (a
@@ -457,16 +461,18 @@ __device__ __forceinline__ void pending_blocks(const float (&w)[16], const float
     n_up = 0;
     n_dn = 0;
     if (!live) return;
-    float amax = 0.0f, hmax = 1.0f;
-    bool h_ok = true;
+    // h on its binary32 bit patterns: every h_j is a non-negative number of at most 2^100
+    // (no sign bit, not NaN) exactly when the largest pattern is at most that of 2^100, and the
+    // largest pattern is then the largest h_j
+    float amax = 0.0f;
+    uint32_t hbits = 0u;
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
         amax = fmaxf(amax, fabsf(w[j]));
-        if (WMSE) {
-            hmax = fmaxf(hmax, h[j]);
-            h_ok = h_ok && h[j] >= 0.0f && h[j] <= 0x1p100f;
-        }
+        if (WMSE) hbits = max(hbits, __float_as_uint(h[j]));
     }
+    const bool h_ok = hbits <= 0x71800000u;     // the pattern of 2^100
+    const float hmax = fmaxf(1.0f, __uint_as_float(hbits));
     const float scale_ref = amax * (1.0f + hmax);
     const int up = c0 + 16, dn = c0 - 1;
     const int all_up = up <= 126 ? (126 - up) / kBlockCodes + 1 : 0;
