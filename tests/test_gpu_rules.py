@@ -141,12 +141,15 @@ def test_window_and_exhaustive_fused(nv, rules, dtype, rule):
 
 
 def test_fused_overflow_negative_h_and_tiny_scale(nv):
-    """The fused launch where losses overflow, where negative h turns the pruning off, and with
-    a global scale whose lowest codes are subnormal (no octave identity)."""
+    """The fused launch where losses overflow, where negative h, h = -0.0 or h above 2^100 turn
+    the pruning off, and with a global scale whose lowest codes are subnormal (no octave
+    identity)."""
     W, h = _inputs(48, 256, torch.float32, seed=55)
     W[:16] *= 1e4
     h[:64] = 3e38
     h[100:140] *= -1.0
+    h[160:176] = -0.0
+    h[192:200] = 2.0 ** 101
     S = nv.global_scale(W, nv.GS_AMAX_448)
     _check(nv, W, h, S, [(1, -9, 6, False), (1, 0, 0, True)], "fused overflow")
     Wt, ht = _inputs(32, 128, torch.float32, seed=57)
@@ -181,6 +184,7 @@ def test_scored_count(nv):
             assert n < 126 * live          # the bounds prune something on these weights
     neg = -h
     assert nv.scale_search_scored(W, neg, S, nv.WMSE, -8) == 126 * live
+    assert nv.scale_search_scored(W, torch.full_like(h, -0.0), S, nv.WMSE, -8) == 126 * live
     # the count accumulates
     c = torch.full((1,), 5, dtype=torch.int64, device=DEV)
     nv.nvfp4_scale_search_scored(W, 1, 152, 288, 288, 0, 16, h, 0, nv.WMSE, -8, S, c)
