@@ -345,9 +345,9 @@ __device__ __forceinline__ float bound_above(const float (&w)[16], const float (
 }
 
 // N codes c0 .. c0 + N - 1 of one lane, each on its own and in ascending order; codes outside
-// 1..126 are skipped. The caller starts the running minimum at (+inf, the first code in range),
-// so a strictly smaller loss replaces it and the result is the scan's first minimum, as on
-// (loss, code) lexicographically.
+// 1..126 are skipped. The caller starts the running minimum at (+inf, the first code in range)
+// and a strictly smaller loss replaces it, so the result is the scan's first minimum, which is
+// the lexicographic minimum of (loss, code).
 template <bool WMSE, int N>
 __device__ __forceinline__ void scan_codes(const float (&w)[16], const float (&h)[16],
                                            const float2* __restrict__ tab, int c0, float& best,
@@ -377,9 +377,8 @@ constexpr int kBlockCodes = 4;
 //     rounding of the binary32 loss tree and of the bound itself (each at most about 20
 //     roundings of 2^-24 on sums of non-negative terms). The test is used only where that
 //     error analysis holds: every h_j without sign bit and at most 2^100, a best loss of at
-//     least 2^-100 and
-//     amax (1 + max h) <= 2^100 best, so that underflowing products (absolute error 2^-150
-//     each) stay far below the margin; elsewhere the lane needs every block.
+//     least 2^-100 and amax (1 + max h) <= 2^100 best, so that underflowing products (absolute
+//     error 2^-150 each) stay far below the margin; elsewhere the lane needs every block.
 //  2. The workgroup's pending blocks are dealt over its lanes, 64 items per wave and round (a
 //     prefix of the per-lane counts in LDS tells each item's owner), so that the workgroup runs
 //     ceil(total / 64) wave-rounds of kBlockCodes codes instead of as many rounds as its busiest
