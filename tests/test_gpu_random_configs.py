@@ -2,6 +2,8 @@
 objectives, windows (including one-sided and wide ones), exhaustive mode, both global-scale
 rules, weight scales over twelve decades, heavy tails, zero and subnormal-range groups, and h
 with zeros and a wide spread. Every output is compared with the oracle bit for bit."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -107,3 +109,16 @@ def test_random_rule_pairs(nv, i):
                           "wmse" if wm else "mse", lo, hi, exh)
         assert_same(g, o, f"rule case {i}: {tuple(W.shape)} {W.dtype} rules {rules}, "
                           f"rule ({obj}, {lo}, {hi}, {exh})")
+
+
+def test_random_sweep(nv):
+    """The two generators above over many more seeds, opt-in: NVFP4_SWEEP_CASES=n runs n random
+    configurations and n / 2 rule pairs (seeds past the parametrised ones), each bit for bit
+    against the oracle."""
+    n = int(os.environ.get("NVFP4_SWEEP_CASES", "0"))
+    if n <= 0:
+        pytest.skip("opt-in: set NVFP4_SWEEP_CASES to the number of configurations")
+    for i in range(1000, 1000 + n):
+        test_random_configuration(nv, i)
+    for i in range(2000, 2000 + n // 2):
+        test_random_rule_pairs(nv, i)
